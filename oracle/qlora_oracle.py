@@ -1,0 +1,378 @@
+"""Plain CPU oracle for the QLoRA adapted-linear hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: it is used by ``tests/``, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of ``bench.py`` and nowhere else.  It shares
+no code, table or constant with the HIP library; the NF4 levels, the
+thresholds and the 8-bit-float codebook are re-derived here from the pages'
+definitions every time the module is imported.
+
+Sources (the text of five web pages on QLoRA):
+  [P1] "QLoRA: Efficient Fine-Tuning" (beta.fermi.ai wiki)
+  [P2] "How QLoRA Fine-Tunes Large Models on Small GPUs: 4-bit Basics"
+  [P3] "What is QLoRA?" (aquanode GPU glossary)
+  [P4] "QLoRA & 4-bit Fine-Tuning" (prepfeed)
+  [P5] "quantized low-rank adaptation (QLoRA)" (Real Python glossary)
+
+What is computed, step by step (numpy; float64 unless a step fixes fp32):
+  nf4_levels / nf4_table   [P1] Step 1, Eq. 2 (levels), Eq. 1 (range [-1, 1])
+  block absmax c1          [P1] Step 1, Eq. 1 with alpha = 1; block of 64
+                           weights from [P3] "The three pieces" and [P4]
+                           Innovation 2
+  encode                   [P1] Step 1, text under Eq. 1 ("snapped to the
+                           nearest NF4 quantile level")
+  double quantization      [P1] Step 2; [P4] Innovation 2 (c1 -> 8-bit float
+                           with a second scale c2, blocks of 256)
+  dequantization           [P1] Step 3 symbols (W0 dequantized to BF16 at
+                           run time); [P3] "The three pieces"
+  forward                  [P1] Step 3, Eq. 3 with the alpha/r scale of the
+                           code snippet's LoraConfig comment
+  backward                 [P1] Step 4, Eq. 5 (adapter gradients), and the
+                           chain rule of the forward for grad_x
+
+Readings taken where the pages are silent or garbled (each is listed, with
+its reason, in the design notes of the repository):
+  * levels are divided by q_16 so the table spans exactly [-1, 1]
+  * thresholds are fp32 midpoints of adjacent levels; ties go to the lower
+    code (strict ">" count)
+  * blocks are 64 consecutive elements of the row-major (out x in) weight
+  * the 8-bit float is OCP E4M3FN, round to nearest, ties to even
+  * c2 is the plain fp32 max of the 256 c1 values of its group
+  * an all-zero block has c1 = 0, every normalized weight is 0 (code 7)
+  * the code of element 2k sits in the low nibble of byte k
+  * s = alpha / r multiplies every adapter term, gradients included
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+closed forms, worked examples printed on the pages, brute force on small
+inputs and automatic differentiation.  The values of h and of the gradients
+for a given input are fixed by no printed example on the pages; they are
+pinned by the identities (B = 0, W0 = 0, merge, autograd, finite
+differences) only.
+"""
+
+from __future__ import annotations
+
+import math
+import statistics
+
+import numpy as np
+
+BLOCK = 64            # weights per first-level absmax block  ([P3], [P4])
+DQ_BLOCKS = 256       # first-level constants per second-level group ([P1] Step 2)
+GROUP = BLOCK * DQ_BLOCKS
+
+
+# --------------------------------------------------------------------------
+# NF4 code table  ([P1] Step 1, Eq. 2; range from the text under Eq. 1)
+# --------------------------------------------------------------------------
+
+def nf4_levels(k: int = 4) -> np.ndarray:
+    """Unnormalized levels q_i = Phi^-1((i - 1/2) / 2^k), i = 1..2^k, float64.
+
+    [P1] Step 1, Eq. 2.  Phi^-1 is the standard normal quantile function,
+    evaluated with ``statistics.NormalDist.inv_cdf``.
+    """
+    nd = statistics.NormalDist(0.0, 1.0)
+    n = 2 ** k
+    return np.array([nd.inv_cdf((i - 0.5) / n) for i in range(1, n + 1)], dtype=np.float64)
+
+
+def nf4_table():
+    """Return (Q, T): 16 fp32 levels spanning [-1, 1] and 15 fp32 thresholds.
+
+    Q_j = fl32(q_{j+1} / q_16): the normalized weight of Eq. 1 lies in
+    [-1, 1] ([P1] Step 1), so the Eq. 2 levels are scaled by their largest
+    value to span exactly that range.
+    T_j = fl32((Q_j + Q_{j+1}) / 2): the midpoint between adjacent levels,
+    formed exactly in float64 and rounded once; a weight is "snapped to the
+    nearest" level ([P1] Step 1) by counting the thresholds below it.
+    """
+    q = nf4_levels(4)
+    Q = (q / q[-1]).astype(np.float32)
+    T = ((Q[:-1].astype(np.float64) + Q[1:].astype(np.float64)) / 2.0).astype(np.float32)
+    return Q, T
+
+
+NF4_Q, NF4_T = nf4_table()
+
+
+# --------------------------------------------------------------------------
+# The 8-bit float used for the double-quantized constants
+# ([P1] Step 2 "8-bit floats"; [P1] figure "scales stored in FP8";
+#  [P4] Innovation 2 "from FP32 down to FP8").  Reading: OCP E4M3FN.
+# --------------------------------------------------------------------------
+
+def e4m3_decode(code) -> np.ndarray:
+    """Exact value of E4M3FN codes (bias 7, 3 mantissa bits, no infinities).
+
+    Exponent field 0 is subnormal: m * 2^-9.  Otherwise 2^(e-7) * (1 + m/8).
+    Codes 0x7F and 0xFF are NaN.
+    """
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, 2.0 ** (e.astype(np.float64) - 7.0) * (1.0 + m / 8.0))
+    mag = np.where((code & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS_CODES = np.arange(0, 0x7F, dtype=np.int64)        # 0x00 .. 0x7E, all finite
+_E4M3_POS_VALUES = e4m3_decode(_E4M3_POS_CODES)              # strictly increasing
+
+
+def e4m3_encode_rne(v) -> np.ndarray:
+    """Nearest E4M3FN code to each non-negative finite v, ties to even code.
+
+    Written as a plain search over the 127 finite non-negative codes: take
+    the code whose exact value is nearest to v (in float64, which holds the
+    fp32 input and every code value exactly); at an exact tie take the code
+    with an even mantissa.  Values above 448 saturate to 448 (never reached
+    on this path, where v <= 1).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(v < 0) or not np.all(np.isfinite(v)):
+        raise ValueError("e4m3_encode_rne expects finite non-negative values")
+    vals = _E4M3_POS_VALUES
+    hi = np.searchsorted(vals, v, side="left")             # vals[hi-1] < v <= vals[hi]
+    hi = np.clip(hi, 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo = np.abs(v - vals[lo])
+    d_hi = np.abs(vals[hi] - v)
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((_E4M3_POS_CODES[hi] & 1) == 0))
+    code = np.where(pick_hi, _E4M3_POS_CODES[hi], _E4M3_POS_CODES[lo])
+    return code.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# bfloat16 rounding (round to nearest, ties to even), written out
+# --------------------------------------------------------------------------
+
+def bf16_bits_rne(x) -> np.ndarray:
+    """bf16 bit patterns of fp32 values, round to nearest with ties to even.
+
+    The two bf16 neighbours of x are its truncation toward zero and the next
+    bf16 away from zero; pick the nearer in exact float64 arithmetic, and on
+    an exact tie the one whose last kept bit is 0.  Zeros keep their sign.
+    Finite inputs only (overflow past the largest bf16 rounds to infinity).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lo_bits = bits & 0xFFFF0000
+    hi_bits = lo_bits + 0x10000
+    lo = lo_bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    hi = hi_bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    xd = x.astype(np.float64)
+    d_lo = np.abs(xd - lo)
+    d_hi = np.abs(hi - xd)
+    lo_even = ((lo_bits >> 16) & 1) == 0
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even)
+    out = np.where(take_hi, hi_bits, lo_bits) >> 16
+    return out.astype(np.uint16)
+
+
+def bf16_bits_to_float64(b) -> np.ndarray:
+    """Exact value of bf16 bit patterns."""
+    b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Quantizer: blockwise NF4 with double quantization
+# --------------------------------------------------------------------------
+
+def quantize_nf4_dq(W) -> dict:
+    """Quantize a weight matrix (any shape, fp32) in row-major order.
+
+    Steps, in the pages' order:
+      1. c1_b = max |w| over block b (64 consecutive weights)      [P1] Eq. 1
+      2. w_hat = fl32(w / c1_b) (alpha = 1); an all-zero block gives 0
+      3. code = number of thresholds T_j strictly below w_hat      [P1] Step 1
+      4. byte k holds the codes of elements 2k (low) and 2k+1 (high)
+      5. c2_g = max c1 over group g of 256 blocks                   [P1] Step 2
+      6. a_b = E4M3(fl32(c1_b / c2_g)); a zero group gives a_b = 0  [P4] Innov. 2
+    The element count must be a multiple of 64; the last group may hold
+    fewer than 256 blocks.
+    Returns dict(codes=uint8[numel/2], absmax8=uint8[numel/64],
+                 c2=float32[ceil(numel/16384)], c1=float32[numel/64]).
+    """
+    w = np.ascontiguousarray(W, dtype=np.float32).reshape(-1)
+    if w.size % BLOCK:
+        raise ValueError("element count must be a multiple of 64")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("weights must be finite")
+    nblk = w.size // BLOCK
+    wb = w.reshape(nblk, BLOCK)
+    c1 = np.max(np.abs(wb), axis=1).astype(np.float32)                      # step 1
+    safe = np.where(c1 > 0, c1, np.float32(1.0)).astype(np.float32)
+    w_hat = (wb / safe[:, None]).astype(np.float32)                         # step 2
+    w_hat = np.where(c1[:, None] > 0, w_hat, np.float32(0.0))
+    codes = np.zeros(wb.shape, dtype=np.uint8)
+    for t in NF4_T:                                                         # step 3
+        codes += (w_hat > t).astype(np.uint8)
+    flat = codes.reshape(-1)
+    packed = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)              # step 4
+    ngrp = (nblk + DQ_BLOCKS - 1) // DQ_BLOCKS
+    c2 = np.zeros(ngrp, dtype=np.float32)
+    for g in range(ngrp):                                                   # step 5
+        c2[g] = np.max(c1[g * DQ_BLOCKS:(g + 1) * DQ_BLOCKS])
+    c2_of_block = np.repeat(c2, DQ_BLOCKS)[:nblk]
+    ratio = np.where(c2_of_block > 0,
+                     (c1 / np.where(c2_of_block > 0, c2_of_block, np.float32(1.0))).astype(np.float32),
+                     np.float32(0.0))
+    absmax8 = e4m3_encode_rne(ratio)                                        # step 6
+    return dict(codes=packed, absmax8=absmax8, c2=c2, c1=c1)
+
+
+def unpack_codes(codes, numel: int) -> np.ndarray:
+    """Nibble codes of each element, element 2k from the low nibble of byte k."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(numel, dtype=np.uint8)
+    out[0::2] = codes[: numel // 2] & 0xF
+    out[1::2] = codes[: numel // 2] >> 4
+    return out
+
+
+def block_scales(absmax8, c2, nblk: int) -> np.ndarray:
+    """s_b = fl32(dec(a_b) * c2_g): the reconstructed first-level constants."""
+    dec = e4m3_decode(np.asarray(absmax8)[:nblk]).astype(np.float32)
+    c2_of_block = np.repeat(np.asarray(c2, dtype=np.float32), DQ_BLOCKS)[:nblk]
+    return (dec * c2_of_block).astype(np.float32)
+
+
+def dequant_nf4_dq(codes, absmax8, c2, numel: int, first_element: int = 0) -> np.ndarray:
+    """bf16 bit patterns of W' = bf16(fl32(Q[code] * s_b)).
+
+    [P1] Step 3 symbols: W0 is dequantized to BF16 at run time.
+    ``codes``/``absmax8`` may describe a contiguous slice of a larger weight:
+    ``first_element`` is that slice's offset in the full weight (a multiple
+    of 64) so the right c2 group is used; ``c2`` is the full c2 array.
+    """
+    if first_element % BLOCK or numel % BLOCK:
+        raise ValueError("slices must be whole 64-element blocks")
+    nblk = numel // BLOCK
+    b0 = first_element // BLOCK
+    grp = (b0 + np.arange(nblk)) // DQ_BLOCKS
+    dec = e4m3_decode(np.asarray(absmax8)[:nblk]).astype(np.float32)
+    s = (dec * np.asarray(c2, dtype=np.float32)[grp]).astype(np.float32)
+    q = NF4_Q[unpack_codes(codes, numel)].reshape(nblk, BLOCK)
+    vals = (q * s[:, None]).astype(np.float32)
+    return bf16_bits_rne(vals.reshape(-1))
+
+
+def dequant_rows(qw: dict, m: int, n: int, rows) -> np.ndarray:
+    """float64 values of W' for the given output rows of an m x n weight."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), n), dtype=np.float64)
+    for i, r in enumerate(rows):
+        e0 = int(r) * n
+        out[i] = bf16_bits_to_float64(dequant_nf4_dq(
+            qw["codes"][e0 // 2:(e0 + n) // 2], qw["absmax8"][e0 // BLOCK:(e0 + n) // BLOCK],
+            qw["c2"], n, first_element=e0))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Adapted linear layer, forward and backward, float64
+# --------------------------------------------------------------------------
+
+def linear_fwd(x, Wd, A, B, s: float):
+    """h = x W'^T + s (x A^T) B^T, and u = x A^T.   [P1] Step 3, Eq. 3.
+
+    x: M x n, Wd (= W', dequantized): m x n, A: r x n, B: m x r, all float64.
+    Eq. 3 writes the layer as h = W0 x + B A x for one column x; with the
+    tokens as the rows of x that is h = x W0^T + x A^T B^T.  The adapter term
+    carries s = alpha / r (the code snippet's LoraConfig comment).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    u = x @ np.asarray(A, dtype=np.float64).T
+    h = x @ np.asarray(Wd, dtype=np.float64).T + s * (u @ np.asarray(B, dtype=np.float64).T)
+    return h, u
+
+
+def linear_bwd(x, g, Wd, A, B, s: float, u=None):
+    """Gradients of <g, h> for the forward above, float64.
+
+    [P1] Step 4, Eq. 5: dL/dA = B^T (dL/dh) x^T and dL/dB = (dL/dh)(A x)^T,
+    here with tokens as rows and the s factor: grad_A = s v^T x,
+    grad_B = s g^T u, with v = g B and u = x A^T.  The input gradient follows
+    the chain rule through the frozen W': grad_x = g W' + s v A (W0 itself
+    gets no gradient).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    if u is None:
+        u = x @ A.T
+    v = g @ B
+    grad_x = g @ np.asarray(Wd, dtype=np.float64) + s * (v @ A)
+    grad_A = s * (v.T @ x)
+    grad_B = s * (g.T @ u)
+    return dict(grad_x=grad_x, grad_A=grad_A, grad_B=grad_B, v=v)
+
+
+def linear_fwd_loops(x, Wd, A, B, s: float):
+    """Same as linear_fwd with explicit Python loops (small inputs only)."""
+    M, n = len(x), len(x[0])
+    m, r = len(Wd), len(A)
+    u = [[math.fsum(float(x[t][k]) * float(A[q][k]) for k in range(n)) for q in range(r)] for t in range(M)]
+    h = [[math.fsum(float(x[t][k]) * float(Wd[j][k]) for k in range(n))
+          + s * math.fsum(u[t][q] * float(B[j][q]) for q in range(r)) for j in range(m)] for t in range(M)]
+    return np.array(h), np.array(u)
+
+
+def linear_bwd_loops(x, g, Wd, A, B, s: float):
+    """Same as linear_bwd with explicit Python loops (small inputs only)."""
+    M, n = len(x), len(x[0])
+    m, r = len(Wd), len(A)
+    u = [[math.fsum(float(x[t][k]) * float(A[q][k]) for k in range(n)) for q in range(r)] for t in range(M)]
+    v = [[math.fsum(float(g[t][j]) * float(B[j][q]) for j in range(m)) for q in range(r)] for t in range(M)]
+    gx = [[math.fsum(float(g[t][j]) * float(Wd[j][k]) for j in range(m))
+           + s * math.fsum(v[t][q] * float(A[q][k]) for q in range(r)) for k in range(n)] for t in range(M)]
+    gA = [[s * math.fsum(v[t][q] * float(x[t][k]) for t in range(M)) for k in range(n)] for q in range(r)]
+    gB = [[s * math.fsum(float(g[t][j]) * u[t][q] for t in range(M)) for q in range(r)] for j in range(m)]
+    return dict(grad_x=np.array(gx), grad_A=np.array(gA), grad_B=np.array(gB))
+
+
+# --------------------------------------------------------------------------
+# Storage arithmetic  ([P3] "The three pieces", worked example; [P4] Innov. 2)
+# --------------------------------------------------------------------------
+
+def storage_bytes(numel: int) -> int:
+    """Bytes of codes + 8-bit constants + fp32 c2 for one quantized weight."""
+    nblk = numel // BLOCK
+    return numel // 2 + nblk + 4 * ((nblk + DQ_BLOCKS - 1) // DQ_BLOCKS)
+
+
+def constant_overhead_bits(double_quant: bool) -> float:
+    """Bits per parameter spent on scale constants.
+
+    Without double quantization: one fp32 per 64 weights.  With it: one
+    8-bit float per 64 weights plus one fp32 per 64 * 256 weights.
+    """
+    if not double_quant:
+        return 32.0 / BLOCK
+    return 8.0 / BLOCK + 32.0 / (BLOCK * DQ_BLOCKS)
+
+
+def adapter_params(m: int, n: int, r: int) -> int:
+    """r (m + n): trainable parameters of one adapted m x n layer ([P1] Eq. 4)."""
+    return r * (m + n)
+
+
+# --------------------------------------------------------------------------
+# Comparison point: plain 4-bit integer absmax quantization ([P1] Step 1 and
+# [P4] Innovation 1 contrast NF4 with uniformly spaced INT4 levels)
+# --------------------------------------------------------------------------
+
+def int4_absmax_roundtrip(W) -> np.ndarray:
+    """Round trip through symmetric INT4 absmax quantization, blocks of 64.
+
+    Levels k/7 * c1, k = -7..7 (uniform spacing), nearest level, fp32 c1.
+    """
+    w = np.asarray(W, dtype=np.float64).reshape(-1, BLOCK)
+    c1 = np.max(np.abs(w), axis=1, keepdims=True)
+    safe = np.where(c1 > 0, c1, 1.0)
+    k = np.clip(np.rint(w / safe * 7.0), -7, 7)
+    return (k / 7.0 * c1).reshape(-1)
