@@ -1,0 +1,21 @@
+"""MI355X-native QLoRA adapted-linear hot path (NF4 + double quantization + LoRA).
+
+The compute lives in libqlora.so (hand-written HIP for gfx950, C ABI in
+include/qlora.h); this package is a thin torch binding over it.
+"""
+
+from .api import (  # noqa: F401
+    QLORA_OP_BWD,
+    QLORA_OP_FWD,
+    QuantizedWeight,
+    alloc_quantized,
+    dequant_nf4_dq,
+    linear_bwd,
+    linear_fwd,
+    nf4_table,
+    profile_enable,
+    profile_query,
+    quantize_nf4_dq,
+    workspace_bytes,
+)
+from ._lib import LIB_PATH, QloraError  # noqa: F401

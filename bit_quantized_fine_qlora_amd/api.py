@@ -1,0 +1,158 @@
+"""Torch-facing binding of the QLoRA library.
+
+Only marshals tensors into pointers and sizes and passes the current HIP
+stream; every step of the computation runs in the HIP kernels of
+libqlora.so.  Torch supplies device memory (outputs and workspaces).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+
+QLORA_OP_FWD = 0
+QLORA_OP_BWD = 1
+
+
+@dataclasses.dataclass
+class QuantizedWeight:
+    """NF4 + double-quantized m x n weight: codes, absmax8 (E4M3) and c2."""
+    codes: torch.Tensor     # uint8 [m*n/2]
+    absmax8: torch.Tensor   # uint8 [m*n/64]
+    c2: torch.Tensor        # float32 [ceil(m*n/16384)]
+    m: int
+    n: int
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.absmax8.numel() + 4 * self.c2.numel()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def nf4_table():
+    """(levels[16], thresholds[15]) as the library derived them (host)."""
+    lib = _lib.load()
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    lib.qlora_nf4_table(ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p))
+    return list(lv), list(th)
+
+
+def workspace_bytes(op: int, M: int, n: int, m: int, r: int) -> int:
+    return int(_lib.load().qlora_workspace_bytes(op, M, n, m, r))
+
+
+def alloc_quantized(m: int, n: int, device="cuda") -> QuantizedWeight:
+    numel = m * n
+    return QuantizedWeight(
+        codes=torch.empty(numel // 2, dtype=torch.uint8, device=device),
+        absmax8=torch.empty(numel // 64, dtype=torch.uint8, device=device),
+        c2=torch.empty((numel // 64 + 255) // 256, dtype=torch.float32, device=device),
+        m=m, n=n)
+
+
+def quantize_nf4_dq(W: torch.Tensor, out: QuantizedWeight | None = None) -> QuantizedWeight:
+    m, n = W.shape
+    _need(W, torch.float32, (m, n), "W")
+    q = out if out is not None else alloc_quantized(m, n, W.device)
+    st = _lib.load().qlora_quantize_nf4_dq(_ptr(W), m, n, _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2),
+                                           _stream(W.device))
+    _lib.check(st, "qlora_quantize_nf4_dq")
+    return q
+
+
+def dequant_nf4_dq(q: QuantizedWeight) -> torch.Tensor:
+    out = torch.empty((q.m, q.n), dtype=torch.bfloat16, device=q.codes.device)
+    st = _lib.load().qlora_dequant_nf4_dq(_ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2), q.m, q.n, _ptr(out),
+                                          _stream(q.codes.device))
+    _lib.check(st, "qlora_dequant_nf4_dq")
+    return out
+
+
+def _workspace(op, M, n, m, r, device, workspace):
+    need = workspace_bytes(op, M, n, m, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def linear_fwd(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
+               h: torch.Tensor | None = None, u: torch.Tensor | None = None, want_u: bool = True,
+               workspace: torch.Tensor | None = None):
+    """h = x W'^T + s (x A^T) B^T.  Returns (h bf16 [M, m], u fp32 [M, r] or None)."""
+    M, n = x.shape
+    m = q.m
+    r = A.shape[0]
+    _need(x, torch.bfloat16, (M, q.n), "x")
+    _need(A, torch.bfloat16, (r, q.n), "A")
+    _need(B, torch.bfloat16, (m, r), "B")
+    if h is None:
+        h = torch.empty((M, m), dtype=torch.bfloat16, device=x.device)
+    if u is None and want_u:
+        u = torch.empty((M, r), dtype=torch.float32, device=x.device)
+    ws = _workspace(QLORA_OP_FWD, M, n, m, r, x.device, workspace)
+    st = _lib.load().qlora_linear_fwd(M, n, m, r, float(s), _ptr(x), _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2),
+                                      _ptr(A), _ptr(B), _ptr(h), _ptr(u), _ptr(ws), ws.numel(), _stream(x.device))
+    _lib.check(st, "qlora_linear_fwd")
+    return h, u
+
+
+def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
+               u: torch.Tensor | None = None, need_grad_x: bool = True, out=None,
+               workspace: torch.Tensor | None = None):
+    """Returns (grad_x bf16 [M, n] or None, grad_A bf16 [r, n], grad_B bf16 [m, r])."""
+    M, n = x.shape
+    m = q.m
+    r = A.shape[0]
+    _need(x, torch.bfloat16, (M, q.n), "x")
+    _need(g, torch.bfloat16, (M, m), "g")
+    _need(A, torch.bfloat16, (r, n), "A")
+    _need(B, torch.bfloat16, (m, r), "B")
+    if u is not None:
+        _need(u, torch.float32, (M, r), "u")
+    if out is None:
+        gx = torch.empty((M, n), dtype=torch.bfloat16, device=x.device) if need_grad_x else None
+        gA = torch.empty((r, n), dtype=torch.bfloat16, device=x.device)
+        gB = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
+    else:
+        gx, gA, gB = out
+    ws = _workspace(QLORA_OP_BWD, M, n, m, r, x.device, workspace)
+    st = _lib.load().qlora_linear_bwd(M, n, m, r, float(s), _ptr(x), _ptr(g), _ptr(q.codes), _ptr(q.absmax8),
+                                      _ptr(q.c2), _ptr(A), _ptr(B), _ptr(u), _ptr(gx), _ptr(gA), _ptr(gB), _ptr(ws),
+                                      ws.numel(), _stream(x.device))
+    _lib.check(st, "qlora_linear_bwd")
+    return gx, gA, gB
+
+
+def profile_enable(on: bool = True) -> None:
+    _lib.check(_lib.load().qlora_profile_enable(1 if on else 0), "qlora_profile_enable")
+
+
+def profile_query(name: str):
+    """(launches, total_ms) of a kernel recorded while profiling was on."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _lib.check(_lib.load().qlora_profile_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)),
+               "qlora_profile_query")
+    return int(n.value), float(ms.value)

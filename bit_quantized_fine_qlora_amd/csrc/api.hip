@@ -1,0 +1,363 @@
+// C ABI of the QLoRA adapted-linear library: argument checks, workspace
+// layout, kernel dispatch and optional kernel timing.  Declared in qlora.h.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/qlora.h"
+#include "qlora_common.h"
+
+namespace qlora {
+
+// kernels (defined in the other translation units)
+void launch_quantize(const float* W, int64_t numel, uint8_t* codes, uint8_t* absmax8, float* c2,
+                     const Nf4Table& tab, hipStream_t stream);
+void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t numel, uint16_t* out,
+                    const Nf4Table& tab, hipStream_t stream);
+void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                     const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
+                     float s, const Nf4Table& tab, hipStream_t stream);
+void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m, int r,
+                       float s, const Nf4Table& tab, hipStream_t stream);
+int skinny_splits(int64_t M, int64_t K);
+int64_t skinny_kc(int64_t K, int splits);
+void launch_skinny_nt(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
+                      float* out, hipStream_t stream);
+int grad_splits(int64_t M, int64_t J);
+int64_t grad_tc(int64_t M, int splits);
+void launch_lora_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, float s, int splits,
+                      float* part, int transpose_out, uint16_t* out, hipStream_t stream);
+void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t stream);
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// NF4 table: Phi^-1 by bisection on Phi(x) = erfc(-x/sqrt2)/2 in double,
+// polished by Newton steps, then normalized by the largest level.
+// ---------------------------------------------------------------------------
+double normal_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double normal_quantile(double p) {
+  double lo = -12.0, hi = 12.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (normal_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  double x = 0.5 * (lo + hi);
+  for (int it = 0; it < 3; ++it) {
+    const double pdf = std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+    x -= (normal_cdf(x) - p) / pdf;
+  }
+  return x;
+}
+
+Nf4Table build_table() {
+  Nf4Table t;
+  double q[16];
+  for (int i = 1; i <= 16; ++i) q[i - 1] = normal_quantile((i - 0.5) / 16.0);
+  for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
+  // exact symmetry of the construction, kept exact after rounding
+  for (int j = 0; j < 8; ++j) t.q[j] = -t.q[15 - j];
+  for (int j = 0; j < 15; ++j) t.t[j] = (float)(((double)t.q[j] + (double)t.q[j + 1]) * 0.5);
+  return t;
+}
+
+const Nf4Table& table() {
+  static const Nf4Table t = build_table();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct Rec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Rec> g_recs;
+
+struct Timed {
+  hipStream_t s;
+  const char* name;
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  Timed(const char* nm, hipStream_t st) : s(st), name(nm) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+    if (on) {
+      hipEventCreate(&a);
+      hipEventCreate(&b);
+      hipEventRecord(a, s);
+    }
+  }
+  ~Timed() {
+    if (!on) return;
+    hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_recs.push_back(Rec{name, a, b});
+  }
+};
+
+// ---------------------------------------------------------------------------
+// checks
+// ---------------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+qlora_status check_weight_shape(int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0 || (n % kBlock) != 0) return QLORA_ERR_SHAPE;
+  if (m >= kMaxDim || n >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (m > ((int64_t)1 << 40) / n) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+qlora_status check_linear(int64_t M, int64_t n, int64_t m, int32_t r, float s) {
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M >= kMaxDim) return QLORA_ERR_SHAPE;
+  if (M > ((int64_t)1 << 40) / (n > m ? n : m)) return QLORA_ERR_SHAPE;
+  if (r < 1 || r > kMaxRank) return QLORA_ERR_RANK;
+  if (!std::isfinite(s)) return QLORA_ERR_VALUE;
+  return QLORA_OK;
+}
+
+qlora_status hip_status() {
+  return hipGetLastError() == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t total = 0;
+  size_t take(size_t bytes) {
+    const size_t off = total;
+    total += align256(bytes);
+    return off;
+  }
+};
+
+struct FwdWs {
+  size_t part, u, total;
+  int splits;
+};
+
+FwdWs fwd_ws(int64_t M, int64_t n, int32_t r) {
+  WsLayout L;
+  FwdWs w;
+  w.splits = skinny_splits(M, n);
+  w.part = L.take((size_t)w.splits * M * r * sizeof(float));
+  w.u = L.take((size_t)M * r * sizeof(float));
+  w.total = L.total;
+  return w;
+}
+
+struct BwdWs {
+  size_t At, Bt, part_uv, u, v, gA, gB, total;
+  int su, sv, sa, sb;
+};
+
+BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
+  WsLayout L;
+  BwdWs w;
+  w.su = skinny_splits(M, n);
+  w.sv = skinny_splits(M, m);
+  w.sa = grad_splits(M, n);
+  w.sb = grad_splits(M, m);
+  w.At = L.take((size_t)n * r * 2);
+  w.Bt = L.take((size_t)m * r * 2);
+  const int suv = w.su > w.sv ? w.su : w.sv;
+  w.part_uv = L.take((size_t)suv * M * r * sizeof(float));
+  w.u = L.take((size_t)M * r * sizeof(float));
+  w.v = L.take((size_t)M * r * sizeof(float));
+  w.gA = L.take((size_t)w.sa * n * r * sizeof(float));
+  w.gB = L.take((size_t)w.sb * m * r * sizeof(float));
+  w.total = L.total;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(base) + off);
+}
+
+}  // namespace
+}  // namespace qlora
+
+using namespace qlora;
+
+extern "C" {
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "invalid shape (sizes must be positive, n a multiple of 64, within index range)";
+    case QLORA_ERR_RANK: return "rank r must be in 1..128";
+    case QLORA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case QLORA_ERR_HIP: return "a HIP launch failed";
+    case QLORA_ERR_VALUE: return "invalid value (non-finite s or unknown op)";
+    default: return "unknown status";
+  }
+}
+
+int qlora_version(void) { return 100; }
+
+void qlora_nf4_table(float* levels, float* thresholds) {
+  const Nf4Table& t = table();
+  if (levels) std::memcpy(levels, t.q, sizeof(t.q));
+  if (thresholds) std::memcpy(thresholds, t.t, sizeof(t.t));
+}
+
+qlora_status qlora_quantize_nf4_dq(const float* W, int64_t m, int64_t n, uint8_t* codes, uint8_t* absmax8,
+                                   float* c2, qlora_stream_t stream) {
+  if (!W || !codes || !absmax8 || !c2) return QLORA_ERR_NULL;
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2)) return QLORA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("quantize", s);
+    launch_quantize(W, m * n, codes, absmax8, c2, table(), s);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_dequant_nf4_dq(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m,
+                                  int64_t n, qlora_bf16* W_out, qlora_stream_t stream) {
+  if (!codes || !absmax8 || !c2 || !W_out) return QLORA_ERR_NULL;
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(W_out)) return QLORA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("dequant", s);
+    launch_dequant(codes, absmax8, c2, m * n, W_out, table(), s);
+  }
+  return hip_status();
+}
+
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r) {
+  if (check_linear(M, n, m, r, 1.0f) != QLORA_OK) return 0;
+  if (op == QLORA_OP_FWD) return fwd_ws(M, n, r).total;
+  if (op == QLORA_OP_BWD) return bwd_ws(M, n, m, r).total;
+  return 0;
+}
+
+qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                              const uint8_t* codes, const uint8_t* absmax8, const float* c2, const qlora_bf16* A,
+                              const qlora_bf16* B, qlora_bf16* h, float* u_out, void* workspace,
+                              size_t workspace_bytes, qlora_stream_t stream) {
+  qlora_status st = check_linear(M, n, m, r, s);
+  if (st != QLORA_OK) return st;
+  if (!x || !codes || !absmax8 || !c2 || !A || !B || !h) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(A) ||
+      !aligned16(B) || !aligned16(h) || (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  const FwdWs w = fwd_ws(M, n, r);
+  if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float* u = u_out ? u_out : at<float>(workspace, w.u);
+  {
+    Timed tm("skinny_nt", hs);
+    launch_skinny_nt(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs);
+  }
+  {
+    Timed tm("fwd_gemm", hs);
+    launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s, table(), hs);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                              const qlora_bf16* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                              const qlora_bf16* A, const qlora_bf16* B, const float* u, qlora_bf16* grad_x,
+                              qlora_bf16* grad_A, qlora_bf16* grad_B, void* workspace, size_t workspace_bytes,
+                              qlora_stream_t stream) {
+  qlora_status st = check_linear(M, n, m, r, s);
+  if (st != QLORA_OK) return st;
+  if (!x || !g || !codes || !absmax8 || !c2 || !A || !B || !grad_A || !grad_B) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(grad_A) || !aligned16(grad_B) || (u && !aligned16(u)) ||
+      (grad_x && !aligned16(grad_x)))
+    return QLORA_ERR_ALIGN;
+  const BwdWs w = bwd_ws(M, n, m, r);
+  if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float* part = at<float>(workspace, w.part_uv);
+  const float* uu = u;
+  if (!uu) {
+    Timed tm("skinny_nt", hs);
+    launch_skinny_nt(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs);
+    uu = at<float>(workspace, w.u);
+  }
+  uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
+  uint16_t* At = at<uint16_t>(workspace, w.At);
+  float* v = at<float>(workspace, w.v);
+  {
+    Timed tm("transpose", hs);
+    launch_transpose_bf16(B, m, r, Bt, hs);
+  }
+  {
+    Timed tm("skinny_nt", hs);
+    launch_skinny_nt(g, M, m, Bt, r, part, w.sv, v, hs);
+  }
+  {
+    Timed tm("lora_grad", hs);
+    launch_lora_grad(x, M, n, v, r, s, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs);
+  }
+  {
+    Timed tm("lora_grad", hs);
+    launch_lora_grad(g, M, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
+  }
+  if (grad_x) {
+    {
+      Timed tm("transpose", hs);
+      launch_transpose_bf16(A, r, n, At, hs);
+    }
+    Timed tm("dgrad_gemm", hs);
+    launch_dgrad_gemm(g, codes, absmax8, c2, At, v, grad_x, M, n, m, r, s, table(), hs);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) {
+    for (auto& rec : g_recs) {
+      hipEventDestroy(rec.a);
+      hipEventDestroy(rec.b);
+    }
+    g_recs.clear();
+  }
+  g_prof_on = on != 0;
+  return QLORA_OK;
+}
+
+qlora_status qlora_profile_query(const char* name, int64_t* launches, double* total_ms) {
+  if (!name || !launches || !total_ms) return QLORA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t cnt = 0;
+  double tot = 0.0;
+  for (auto& rec : g_recs) {
+    if (rec.name != name) continue;
+    if (hipEventSynchronize(rec.b) != hipSuccess) return QLORA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, rec.a, rec.b) != hipSuccess) return QLORA_ERR_HIP;
+    ++cnt;
+    tot += ms;
+  }
+  *launches = cnt;
+  *total_ms = tot;
+  return QLORA_OK;
+}
+
+}  // extern "C"

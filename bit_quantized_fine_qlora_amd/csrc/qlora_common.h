@@ -1,0 +1,147 @@
+// Shared device-side definitions for the QLoRA HIP kernels (gfx950 only).
+//
+// Data layout (row-major everywhere):
+//   W0      m x n fp32 (out x in); quantized in 64-element blocks that run
+//           along n, 256 blocks (16384 elements) per double-quant group.
+//   codes   m*n/2 bytes, element 2k in the low nibble of byte k.
+//   absmax8 m*n/64 bytes, E4M3FN code of c1_b / c2_g.
+//   c2      ceil(m*n/16384) fp32.
+//   x M x n, g M x m, A r x n, B m x r, h M x m, grad_x M x n: bf16 bits.
+//   u = x A^T and v = g B: M x r fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kBlock = 64;        // weights per absmax block
+constexpr int kGroupBlocks = 256; // blocks per double-quant group
+constexpr int kMaxRank = 128;
+
+// NF4 levels (16, ascending, spanning [-1, 1]) and the 15 midpoints between
+// them, passed by value in kernel arguments.
+struct Nf4Table {
+  float q[16];
+  float t[15];
+};
+
+// E4M3FN (bias 7, 3 mantissa bits) to fp32.  Only non-negative finite codes
+// occur on this path; the value is exact in fp32.
+__device__ __forceinline__ float e4m3_decode(uint32_t a) {
+  const uint32_t e = (a >> 3) & 15u, mnt = a & 7u;
+  const float normal = __uint_as_float(((e + 120u) << 23) | (mnt << 20));
+  const float sub = (float)mnt * 0.001953125f;  // m * 2^-9
+  return e ? normal : sub;
+}
+
+// Round-to-nearest-even E4M3FN code of v in [0, 1] (no saturation needed).
+__device__ __forceinline__ uint32_t e4m3_encode_unit(float v) {
+  if (!(v > 0.0f)) return 0u;
+  const uint32_t b = __float_as_uint(v);
+  int e = (int)(b >> 23) - 127;
+  if (e < -6) {  // subnormal codes are multiples of 2^-9; 8 carries into 0x08
+    return (uint32_t)__builtin_rintf(v * 512.0f);
+  }
+  const uint32_t mant = b & 0x7FFFFFu;
+  uint32_t top = mant >> 20;
+  const uint32_t rest = mant & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (top & 1u))) {
+    ++top;
+    if (top == 8u) { top = 0u; ++e; }
+  }
+  return ((uint32_t)(e + 7) << 3) | top;
+}
+
+// Per-block scale s_b = fl32(dec(a_b) * c2_g).
+__device__ __forceinline__ float block_scale(const uint8_t* absmax8, const float* c2, int64_t blk) {
+  return e4m3_decode(absmax8[blk]) * c2[blk >> 8];
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;  // round to nearest even (v_cvt_pk_bf16_f32)
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 16-entry bf16 lookup table for one block, held as byte planes so that
+// v_perm_b32 can look up four entries at once:
+//   lo[k] holds the low bytes of entries 4k..4k+3, hi[k] their high bytes.
+struct BlockLut {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+// Build the table of W' = bf16(fl32(Q[c] * s)) for c = 0..15.
+__device__ __forceinline__ BlockLut make_block_lut(const Nf4Table& tab, float s) {
+  uint32_t pr[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pr[k] = pack_bf16x2(tab.q[2 * k] * s, tab.q[2 * k + 1] * s);
+  BlockLut L;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // pr[2k] = (e0 | e1 << 16), pr[2k+1] = (e2 | e3 << 16)
+    L.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
+    L.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
+  }
+  return L;
+}
+
+// Dequantize the 8 codes of one 32-bit word (elements e0..e7, e0 in the low
+// nibble) into 4 words of bf16 pairs (e0,e1) (e2,e3) (e4,e5) (e6,e7).
+__device__ __forceinline__ void lut_dequant8(const BlockLut& L, uint32_t w, uint32_t out[4]) {
+  const uint32_t sel_e = w & 0x07070707u;          // even elements: low nibble of each byte
+  const uint32_t sel_o = (w >> 4) & 0x07070707u;   // odd elements: high nibble
+  // byte masks 0xFF where the code is >= 8 (bit 3 of the nibble)
+  const uint32_t te = (w >> 3) & 0x01010101u;
+  const uint32_t to = (w >> 7) & 0x01010101u;
+  const uint32_t me = (te << 8) - te;
+  const uint32_t mo = (to << 8) - to;
+  const uint32_t lo_e = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_e);
+  const uint32_t lo_e8 = __builtin_amdgcn_perm(L.lo[3], L.lo[2], sel_e);
+  const uint32_t hi_e = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_e);
+  const uint32_t hi_e8 = __builtin_amdgcn_perm(L.hi[3], L.hi[2], sel_e);
+  const uint32_t lo_o = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_o);
+  const uint32_t lo_o8 = __builtin_amdgcn_perm(L.lo[3], L.lo[2], sel_o);
+  const uint32_t hi_o = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_o);
+  const uint32_t hi_o8 = __builtin_amdgcn_perm(L.hi[3], L.hi[2], sel_o);
+  const uint32_t LE = (lo_e8 & me) | (lo_e & ~me);  // v_bfi_b32
+  const uint32_t HE = (hi_e8 & me) | (hi_e & ~me);
+  const uint32_t LO = (lo_o8 & mo) | (lo_o & ~mo);
+  const uint32_t HO = (hi_o8 & mo) | (hi_o & ~mo);
+  // low bytes of e0 e1 e2 e3 and of e4 e5 e6 e7, then the high bytes
+  const uint32_t l03 = __builtin_amdgcn_perm(LO, LE, 0x05010400u);
+  const uint32_t l47 = __builtin_amdgcn_perm(LO, LE, 0x07030602u);
+  const uint32_t h03 = __builtin_amdgcn_perm(HO, HE, 0x05010400u);
+  const uint32_t h47 = __builtin_amdgcn_perm(HO, HE, 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(h03, l03, 0x05010400u);
+  out[1] = __builtin_amdgcn_perm(h03, l03, 0x07030602u);
+  out[2] = __builtin_amdgcn_perm(h47, l47, 0x05010400u);
+  out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Split an fp32 value into bf16 hi + lo with hi + lo equal to v to ~2^-16.
+__device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
+  const float h = (float)(__bf16)v;
+  hi = h;
+  lo = v - h;
+}
+
+}  // namespace qlora

@@ -1,0 +1,143 @@
+// Blockwise NF4 quantizer with double quantization, and the bf16 dequantizer.
+//
+// Method: "QLoRA: Efficient Fine-Tuning", Step 1 (Eq. 1 normalization by the
+// block absmax, Eq. 2 normal-quantile levels, snap to the nearest level) and
+// Step 2 (double quantization of the absmax constants to an 8-bit float in
+// blocks of 256); block size 64 from "What is QLoRA?" ("The three pieces")
+// and "QLoRA & 4-bit Fine-Tuning" (Innovation 2).
+#include "qlora_common.h"
+
+namespace qlora {
+
+// fl32(w / c) for |w| <= c, c in [2^-100, 2^100], |w| >= 2^-100, with y the
+// correctly rounded 1/c.  Two fused multiply-add corrections of w*y; the
+// second one starts from a quotient within one ulp, where the remainder
+// w - c*q is exact and one more step rounds correctly (Markstein's
+// reciprocal-based division theorem).
+__device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) {
+  const float q0 = w * y;
+  const float r0 = __builtin_fmaf(-c, q0, w);
+  const float q1 = __builtin_fmaf(r0, y, q0);
+  const float r1 = __builtin_fmaf(-c, q1, w);
+  return __builtin_fmaf(r1, y, q1);
+}
+
+// Code = number of thresholds strictly below the normalized weight.
+__device__ __forceinline__ uint32_t nf4_code(float v, const Nf4Table& tab) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (v > tab.t[j]) ? 1u : 0u;
+  return c;
+}
+
+// One workgroup per double-quant group (256 blocks of 64 weights).  In each
+// of four passes a quad of lanes covers one block, 16 consecutive weights per
+// lane (four 16-byte loads), so a wave reads 4 KB of contiguous weights.
+__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ W, int64_t nblk,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ absmax8,
+                                                               float* __restrict__ c2out, Nf4Table tab) {
+  __shared__ float s_c1[kGroupBlocks];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x;
+  const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
+  const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
+
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lb = pass * 64 + (tid >> 2);
+    const int quarter = tid & 3;
+    const bool valid = lb < nb;
+    float w[16];
+    if (valid) {
+      const float4* src = reinterpret_cast<const float4*>(W + (blk0 + lb) * kBlock + quarter * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 t = src[i];
+        w[4 * i + 0] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    const float c1 = a;
+    if (valid && quarter == 0) s_c1[lb] = c1;
+
+    // Fast path needs every quotient away from underflow; anything else
+    // (zeros, tiny or huge constants) takes the IEEE division.
+    bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) slow |= fabsf(w[i]) < 0x1p-100f;
+    float q[16];
+    if (!slow) {
+      const float y = 1.0f / c1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = div_by_block_absmax(w[i], c1, y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= nf4_code(q[i], tab) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= nf4_code(q[8 + i], tab) << (4 * i);
+    if (valid) {
+      u32x2 pk = {lo, hi};
+      *reinterpret_cast<u32x2*>(codes + (blk0 + lb) * (kBlock / 2) + quarter * 8) = pk;
+    }
+  }
+  __syncthreads();
+
+  // c2 = max of the group's c1; then each block's constant as E4M3(c1 / c2).
+  float c1 = tid < nb ? s_c1[tid] : 0.0f;
+  float m = c1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  if (tid < nb) {
+    const uint32_t code = c2 > 0.0f ? e4m3_encode_unit(c1 / c2) : 0u;
+    absmax8[blk0 + tid] = (uint8_t)code;
+  }
+  if (tid == 0) c2out[blockIdx.x] = c2;
+}
+
+// W' = bf16(fl32(Q[code] * s_b)) for 8 consecutive weights per thread.
+__global__ __launch_bounds__(256) void dequant_nf4_dq_kernel(const uint32_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ absmax8,
+                                                              const float* __restrict__ c2, int64_t nwords,
+                                                              u32x4* __restrict__ out, Nf4Table tab) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nwords) return;
+  const int64_t blk = i >> 3;  // 8 words of codes per 64-weight block
+  const BlockLut L = make_block_lut(tab, block_scale(absmax8, c2, blk));
+  uint32_t o[4];
+  lut_dequant8(L, codes[i], o);
+  out[i] = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+void launch_quantize(const float* W, int64_t numel, uint8_t* codes, uint8_t* absmax8, float* c2,
+                     const Nf4Table& tab, hipStream_t stream) {
+  const int64_t nblk = numel / kBlock;
+  const int64_t ngrp = (nblk + kGroupBlocks - 1) / kGroupBlocks;
+  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)ngrp), dim3(256), 0, stream, W, nblk, codes, absmax8,
+                     c2, tab);
+}
+
+void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t numel, uint16_t* out,
+                    const Nf4Table& tab, hipStream_t stream) {
+  const int64_t nwords = numel / 8;
+  const int64_t grid = (nwords + 255) / 256;
+  hipLaunchKernelGGL(dequant_nf4_dq_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(codes), absmax8, c2, nwords, reinterpret_cast<u32x4*>(out),
+                     tab);
+}
+
+}  // namespace qlora

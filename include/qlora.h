@@ -1,0 +1,166 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA adapted-linear library.
+ *
+ * The library computes the hot path of QLoRA fine-tuning for one linear layer:
+ *   - blockwise NF4 quantization of a frozen weight with double quantization
+ *     of the block constants;
+ *   - the adapted forward  h = x W'^T + s (x A^T) B^T,  W' = dequant(W0);
+ *   - its backward through the frozen 4-bit weight: grad_x, grad_A, grad_B.
+ * Sources are the QLoRA pages cited at each entry point below.
+ *
+ * Conventions for every call:
+ *   - All tensors are dense, row-major, and live in device memory (HBM) of
+ *     the current HIP device, except where a pointer is marked "host".
+ *   - bf16 tensors are passed as raw 16-bit patterns (qlora_bf16).
+ *   - Every base pointer of a device tensor must be 16-byte aligned.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronizes device memory; workspaces are passed in.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream).  Outputs are overwritten, never accumulated into.
+ *   - Argument errors are reported synchronously, before anything is
+ *     launched, and leave every output untouched.  A failed launch returns
+ *     QLORA_ERR_HIP; outputs are then unspecified.
+ *   - Inputs must be finite; non-finite weights or activations give
+ *     unspecified (but memory-safe) results.
+ *   - Calls that share a workspace must be ordered (same stream, or
+ *     synchronized); calls with separate workspaces may overlap.
+ */
+#ifndef QLORA_H_
+#define QLORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t qlora_bf16;                 /* raw bfloat16 bits */
+typedef struct ihipStream_t* qlora_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,      /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = -2,     /* a size <= 0, n % 64 != 0, or an index overflow */
+  QLORA_ERR_RANK = -3,      /* r outside 1..128 */
+  QLORA_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
+  QLORA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
+  QLORA_ERR_HIP = -6,       /* a HIP launch or query failed */
+  QLORA_ERR_VALUE = -7      /* s is not finite, or an unknown op id */
+} qlora_status;
+
+/* Human-readable text of a status code (static storage). */
+const char* qlora_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int qlora_version(void);
+
+/*
+ * The 16 NF4 levels and 15 decision thresholds the library uses (host).
+ * Levels: q_i = Phi^-1((i - 1/2)/16), i = 1..16 ("QLoRA: Efficient
+ * Fine-Tuning", Step 1, Eq. 2), divided by q_16 so they span exactly [-1, 1]
+ * (the normalized weight range of Eq. 1), rounded to fp32.  Thresholds are
+ * the fp32-rounded midpoints of adjacent levels; a normalized weight takes
+ * the code of the number of thresholds strictly below it (ties go to the
+ * lower code).  Derived on the host at load time.
+ * levels: host float[16]; thresholds: host float[15].  Either may be NULL.
+ */
+void qlora_nf4_table(float* levels, float* thresholds);
+
+/*
+ * Quantize an m x n fp32 weight (out x in) to NF4 with double quantization.
+ * "QLoRA: Efficient Fine-Tuning", Step 1 (Eq. 1: divide by the block absmax;
+ * Eq. 2: normal-quantile levels; snap to the nearest level) and Step 2
+ * (the absmax constants quantized again to an 8-bit float in blocks of 256);
+ * block of 64 weights from "What is QLoRA?" ("The three pieces").
+ *   W        device, m*n fp32, row-major; blocks are 64 consecutive elements
+ *            along n, groups are 256 consecutive blocks (16384 elements; the
+ *            last group may be partial).
+ *   codes    device out, m*n/2 bytes; element 2k in the low nibble of byte k.
+ *   absmax8  device out, m*n/64 bytes: E4M3FN (bias 7, RNE) of c1_b / c2_g,
+ *            where c1_b is the fp32 absmax of block b.
+ *   c2       device out, ceil(m*n/16384) fp32: c2_g = max c1_b over group g.
+ * Requires m >= 1, n >= 64, n % 64 == 0.  Output is bit-identical for a
+ * given W (no atomics, no reduction-order dependence).
+ */
+qlora_status qlora_quantize_nf4_dq(const float* W, int64_t m, int64_t n, uint8_t* codes, uint8_t* absmax8,
+                                   float* c2, qlora_stream_t stream);
+
+/*
+ * Dequantize to bf16: W'_e = bf16_rne(fl32(level[code_e] * s_b)) with
+ * s_b = fl32(dec(absmax8_b) * c2_g) ("QLoRA: Efficient Fine-Tuning", Step 3
+ * symbols: W0 is dequantized to BF16 at run time).  This is exactly the
+ * operand the forward and backward kernels build in on-chip memory.
+ *   W_out    device out, m*n bf16.
+ * Same shape rules as qlora_quantize_nf4_dq.
+ */
+qlora_status qlora_dequant_nf4_dq(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m,
+                                  int64_t n, qlora_bf16* W_out, qlora_stream_t stream);
+
+/* Operation ids for qlora_workspace_bytes. */
+#define QLORA_OP_FWD 0
+#define QLORA_OP_BWD 1
+
+/*
+ * Workspace bytes needed by qlora_linear_fwd (op 0) or qlora_linear_bwd
+ * (op 1) for these sizes; 0 on invalid arguments.  The bwd figure assumes u
+ * is recomputed (the most it can need).
+ */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r);
+
+/*
+ * Adapted forward ("QLoRA: Efficient Fine-Tuning", Step 3, Eq. 3, with the
+ * alpha/r scale of the LoraConfig snippet):
+ *   u = x A^T                      (M x r, fp32 accumulation)
+ *   h = bf16(x W'^T + s u B^T)     (M x m)
+ * with W' the dequantized weight (bf16, formed on chip, never in HBM).
+ *   M tokens, n in-features, m out-features, r rank (1..128), s = alpha/r.
+ *   x        device, M x n bf16.
+ *   codes, absmax8, c2: the quantized m x n weight.
+ *   A        device, r x n bf16.      B  device, m x r bf16.
+ *   h        device out, M x m bf16.
+ *   u_out    device out, M x r fp32, or NULL.  Keep it for the backward.
+ *   workspace, workspace_bytes: at least qlora_workspace_bytes(0, ...).
+ */
+qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                              const uint8_t* codes, const uint8_t* absmax8, const float* c2, const qlora_bf16* A,
+                              const qlora_bf16* B, qlora_bf16* h, float* u_out, void* workspace,
+                              size_t workspace_bytes, qlora_stream_t stream);
+
+/*
+ * Backward of the forward above for upstream gradient g = dL/dh
+ * ("QLoRA: Efficient Fine-Tuning", Step 4 and Eq. 5; s from the snippet):
+ *   v      = g B                          (M x r, fp32)
+ *   grad_x = bf16(g W' + s v A)           (M x n)   -- W0 gets no gradient
+ *   grad_A = bf16(s v^T x)                (r x n)
+ *   grad_B = bf16(s g^T u)                (m x r)
+ *   g        device, M x m bf16.
+ *   u        device, M x r fp32 from qlora_linear_fwd, or NULL to recompute.
+ *   grad_x   device out, M x n bf16, or NULL to skip the input gradient.
+ *   grad_A, grad_B  device out (required).
+ * The reductions over tokens use fixed-order fp32 partials: results are
+ * bit-identical run to run.
+ */
+qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                              const qlora_bf16* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                              const qlora_bf16* A, const qlora_bf16* B, const float* u, qlora_bf16* grad_x,
+                              qlora_bf16* grad_A, qlora_bf16* grad_B, void* workspace, size_t workspace_bytes,
+                              qlora_stream_t stream);
+
+/*
+ * Kernel timing (tracing aid, off by default).  While enabled, every kernel
+ * the library launches is bracketed by HIP events on its stream.
+ * qlora_profile_enable(1) clears earlier records; (0) stops recording.
+ * qlora_profile_query waits for the recorded events of kernel `name`
+ * ("quantize", "dequant", "fwd_gemm", "fwd_small", "dgrad_gemm",
+ * "skinny_nt", "lora_grad", "reduce", "transpose") and reports the launch
+ * count and the summed duration in milliseconds (host pointers).
+ */
+qlora_status qlora_profile_enable(int on);
+qlora_status qlora_profile_query(const char* name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H_ */

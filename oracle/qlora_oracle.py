@@ -260,6 +260,19 @@ def dequant_nf4_dq(codes, absmax8, c2, numel: int, first_element: int = 0) -> np
     return bf16_bits_rne(vals.reshape(-1))
 
 
+def dequant_cols(qw: dict, m: int, n: int, cols) -> np.ndarray:
+    """float64 values of W'[:, cols] for an m x n weight (same definition)."""
+    cols = np.asarray(cols, dtype=np.int64)
+    e = (np.arange(m, dtype=np.int64)[:, None] * n + cols[None, :]).reshape(-1)
+    byte = np.asarray(qw["codes"], dtype=np.uint8)[e // 2]
+    code = np.where(e % 2 == 0, byte & 0xF, byte >> 4)
+    blk = e // BLOCK
+    dec = e4m3_decode(np.asarray(qw["absmax8"])[blk]).astype(np.float32)
+    s = (dec * np.asarray(qw["c2"], dtype=np.float32)[blk // DQ_BLOCKS]).astype(np.float32)
+    vals = (NF4_Q[code] * s).astype(np.float32)
+    return bf16_bits_to_float64(bf16_bits_rne(vals)).reshape(m, len(cols))
+
+
 def dequant_rows(qw: dict, m: int, n: int, rows) -> np.ndarray:
     """float64 values of W' for the given output rows of an m x n weight."""
     rows = np.asarray(rows, dtype=np.int64)

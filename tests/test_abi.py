@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+derives the same NF4 table as the oracle, and rejects bad arguments before
+launching anything (these calls never reach the GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import qlora_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_fine_qlora_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libqlora.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_binding_prototypes_cover_header():
+    from bit_quantized_fine_qlora_amd import _lib
+    assert set(declared_functions()) == set(_lib.PROTOTYPES)
+
+
+def test_library_table_matches_oracle(lib):
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    lib.qlora_nf4_table(ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p))
+    got_q = np.frombuffer(lv, dtype=np.float32)
+    got_t = np.frombuffer(th, dtype=np.float32)
+    assert np.array_equal(got_q.view(np.uint32), O.NF4_Q.view(np.uint32))
+    assert np.array_equal(got_t.view(np.uint32), O.NF4_T.view(np.uint32))
+
+
+def test_status_strings(lib):
+    for st in range(-7, 1):
+        assert len(lib.qlora_status_string(st)) >= 2
+    assert lib.qlora_version() >= 100
+
+
+P = ctypes.c_void_p(1 << 20)   # a non-NULL, 16-byte-aligned dummy; never dereferenced on error paths
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_quantize_argument_errors(lib):
+    f = lib.qlora_quantize_nf4_dq
+    assert f(None, 4, 64, P, P, P, None) == -1
+    assert f(P, 4, 60, P, P, P, None) == -2        # n not a multiple of 64
+    assert f(P, 0, 64, P, P, P, None) == -2
+    assert f(P, -3, 64, P, P, P, None) == -2
+    assert f(P, 4, 0, P, P, P, None) == -2
+    assert f(MIS, 4, 64, P, P, P, None) == -4
+    assert f(P, 1 << 31, 64, P, P, P, None) == -2
+
+
+def test_dequant_argument_errors(lib):
+    f = lib.qlora_dequant_nf4_dq
+    assert f(P, P, None, 4, 64, P, None) == -1
+    assert f(P, P, P, 4, 65, P, None) == -2
+    assert f(P, P, P, 4, 64, MIS, None) == -4
+
+
+def fwd(lib, M=32, n=256, m=256, r=8, s=2.0, x=P, A=P, B=P, h=P, u=None, ws=P, wsb=1 << 30):
+    return lib.qlora_linear_fwd(M, n, m, r, s, x, P, P, P, A, B, h, u, ws, wsb, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert fwd(lib, x=None) == -1
+    assert fwd(lib, h=None) == -1
+    assert fwd(lib, n=100) == -2
+    assert fwd(lib, M=0) == -2
+    assert fwd(lib, m=-1) == -2
+    assert fwd(lib, r=0) == -3
+    assert fwd(lib, r=129) == -3
+    assert fwd(lib, s=float("inf")) == -7
+    assert fwd(lib, s=float("nan")) == -7
+    assert fwd(lib, x=MIS) == -4
+    assert fwd(lib, u=MIS) == -4
+    assert fwd(lib, ws=None) == -5
+    need = lib.qlora_workspace_bytes(0, 32, 256, 256, 8)
+    assert need > 0
+    assert fwd(lib, wsb=need - 1) == -5
+
+
+def test_bwd_argument_errors(lib):
+    f = lib.qlora_linear_bwd
+
+    def call(M=32, n=256, m=256, r=8, s=2.0, g=P, gA=P, gB=P, gx=P, ws=P, wsb=1 << 30):
+        return f(M, n, m, r, s, P, g, P, P, P, P, P, None, gx, gA, gB, ws, wsb, None)
+
+    assert call(g=None) == -1
+    assert call(gA=None) == -1
+    assert call(gB=None) == -1
+    assert call(n=32) == -2
+    assert call(r=200) == -3
+    assert call(gx=MIS) == -4
+    need = lib.qlora_workspace_bytes(1, 32, 256, 256, 8)
+    assert call(wsb=need - 1) == -5
+
+
+def test_workspace_sizes(lib):
+    assert lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16) > 0
+    assert lib.qlora_workspace_bytes(1, 4096, 4096, 14336, 16) > lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16)
+    assert lib.qlora_workspace_bytes(0, 32, 100, 256, 8) == 0
+    assert lib.qlora_workspace_bytes(7, 32, 256, 256, 8) == 0
+    assert lib.qlora_workspace_bytes(0, 32, 256, 256, 0) == 0

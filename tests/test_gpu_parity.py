@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bit-exact: quantizer codes, 8-bit constants, c2 and the dequantized bf16
+weight.  Within tolerance (relative L2 <= 1e-2 and max-abs <= 2e-2 max|ref|):
+h, u, grad_x, grad_A, grad_B.  Small and ragged shapes are checked on every
+output; the full-size layers are checked on every quantizer output and on
+sampled rows / columns of the float outputs, computed by the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import qlora_inputs as QI
+from oracle import qlora_oracle as O
+from parity_utils import assert_close, dev_bf16, f64, host_bits, oracle_full, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def Q():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import bit_quantized_fine_qlora_amd as lib
+    lib._lib.load()
+    return lib
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def run_gpu(Q, W, x_bits, g_bits, A_bits, B_bits, s, need_bwd=True):
+    Wd = torch.from_numpy(W).to("cuda")
+    q = Q.quantize_nf4_dq(Wd)
+    x, A, B = dev_bf16(x_bits), dev_bf16(A_bits), dev_bf16(B_bits)
+    h, u = Q.linear_fwd(x, q, A, B, s)
+    out = dict(q=q, h=h, u=u)
+    if need_bwd:
+        g = dev_bf16(g_bits)
+        gx, gA, gB = Q.linear_bwd(x, g, q, A, B, s, u=u)
+        out.update(grad_x=gx, grad_A=gA, grad_B=gB, x=x, g=g, A=A, B=B)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_quantizer(q, qw):
+    assert np.array_equal(q.codes.cpu().numpy(), qw["codes"]), "codes differ"
+    assert np.array_equal(q.absmax8.cpu().numpy(), qw["absmax8"]), "absmax8 differ"
+    assert np.array_equal(q.c2.cpu().numpy().view(np.uint32), qw["c2"].view(np.uint32)), "c2 differ"
+
+
+def check_full(Q, W, inp, s, need_bwd=True, label=""):
+    ref = oracle_full(W, inp["x"], inp["g"] if need_bwd else None, inp["A"], inp["B"], s)
+    say(f"{label} gpu run shape W={W.shape} x={inp['x'].shape} r={inp['A'].shape[0]}")
+    got = run_gpu(Q, W, inp["x"], inp["g"], inp["A"], inp["B"], s, need_bwd)
+    check_quantizer(got["q"], ref["qw"])
+    deq = host_bits(Q.dequant_nf4_dq(got["q"]))
+    want = O.dequant_nf4_dq(ref["qw"]["codes"], ref["qw"]["absmax8"], ref["qw"]["c2"], W.size).reshape(W.shape)
+    assert np.array_equal(deq, want), "dequantized bf16 weight differs"
+    assert_close(f64(host_bits(got["h"])), ref["h"], f"{label} h")
+    assert_close(got["u"].cpu().numpy(), ref["u"], f"{label} u")
+    if need_bwd:
+        assert_close(f64(host_bits(got["grad_x"])), ref["grad_x"], f"{label} grad_x")
+        assert_close(f64(host_bits(got["grad_A"])), ref["grad_A"], f"{label} grad_A")
+        assert_close(f64(host_bits(got["grad_B"])), ref["grad_B"], f"{label} grad_B")
+    return got, ref
+
+
+# ------------------------------------------------------------------ small
+
+def test_config1_full(Q):
+    L = QI.CONFIGS[1]["layers"][0]
+    inp = QI.layer_inputs(1, L)
+    got, ref = check_full(Q, inp["W"], inp, L.s, label="config1")
+    # u recomputed inside the backward gives the same bits
+    say("config1 bwd with u recomputed")
+    gx2, gA2, gB2 = Q.linear_bwd(got["x"], got["g"], got["q"], got["A"], got["B"], L.s, u=None)
+    torch.cuda.synchronize()
+    assert torch.equal(gx2, got["grad_x"]) and torch.equal(gA2, got["grad_A"]) and torch.equal(gB2, got["grad_B"])
+    # determinism: a second run gives identical bits
+    say("config1 determinism")
+    again = run_gpu(Q, inp["W"], inp["x"], inp["g"], inp["A"], inp["B"], L.s)
+    for k in ("h", "u", "grad_x", "grad_A", "grad_B"):
+        assert torch.equal(again[k], got[k]), k
+    # skipping grad_x leaves the adapter gradients unchanged
+    _, gA3, gB3 = Q.linear_bwd(got["x"], got["g"], got["q"], got["A"], got["B"], L.s, u=got["u"],
+                               need_grad_x=False)
+    torch.cuda.synchronize()
+    assert torch.equal(gA3, got["grad_A"]) and torch.equal(gB3, got["grad_B"])
+
+
+RAGGED = [
+    # (M, n, m, r, s)
+    (17, 192, 200, 5, 1.5),
+    (1, 64, 1, 1, 2.0),
+    (300, 320, 300, 128, 0.125),
+    (600, 1024, 700, 16, 2.0),
+    (513, 256, 520, 24, 0.75),
+    (64, 128, 72, 64, 0.25),
+    (257, 448, 259, 7, 3.0),
+]
+
+
+@pytest.mark.parametrize("M,n,m,r,s", RAGGED)
+def test_ragged_shapes(Q, M, n, m, r, s):
+    inp = QI.custom_inputs(seed=M * 7 + m, M=M, n=n, m=m, r=r)
+    check_full(Q, inp["W"], inp, s, label=f"ragged M={M} n={n} m={m} r={r}")
+
+
+def test_adapter_b_zero(Q):
+    # B = 0 (the adapter's initial state): h is the plain dequant GEMM, grad_A is exactly 0
+    inp = QI.custom_inputs(seed=3, M=96, n=256, m=320, r=16)
+    inp["B"] = np.zeros_like(inp["B"])
+    got, ref = check_full(Q, inp["W"], inp, 2.0, label="B=0")
+    assert not torch.any(got["grad_A"].float() != 0)
+
+
+def test_weight_zero_pure_adapter(Q):
+    # W0 = 0: every code is 7 with a zero scale, so h = s u B^T and grad_x = s v A alone
+    inp = QI.custom_inputs(seed=4, M=80, n=192, m=144, r=8)
+    inp["W"] = np.zeros_like(inp["W"])
+    inp["B"] = QI.to_bf16_bits(QI.bf16_bits_as_f32(inp["B"]) * 50.0)
+    got, ref = check_full(Q, inp["W"], inp, 2.0, label="W0=0")
+    assert np.all(O.unpack_codes(got["q"].codes.cpu().numpy(), inp["W"].size) == 7)
+
+
+def test_zero_blocks_and_partial_group(Q):
+    inp = QI.custom_inputs(seed=5, M=40, n=192, m=100, r=4)   # 19200 weights: 1 full + 1 partial group
+    W = inp["W"]
+    W[3, 64:128] = 0.0                 # one all-zero block
+    W[7, :] = 0.0                      # a whole zero row
+    W[9, 5] = 0.0                      # an isolated exact zero
+    check_full(Q, W, inp, 1.0, label="zero blocks")
+
+
+def test_quantizer_threshold_boundaries(Q):
+    # normalized weights placed exactly on, and one ulp around, every threshold,
+    # with random block absmax values; plus tiny and denormal weights
+    rng = np.random.default_rng(21)
+    nblk = 4096
+    W = np.empty((nblk, 64), dtype=np.float32)
+    T = O.NF4_T
+    for b in range(nblk):
+        c = np.float32(np.exp2(rng.uniform(-20, 10)) * (1 + rng.random()))
+        t = T[rng.integers(0, 15, size=63)]
+        k = rng.integers(-2, 3, size=63)
+        tk = (t.view(np.int32) + k.astype(np.int32)).view(np.float32)
+        tk = np.where(t == 0, np.float32(0), tk)
+        sign = np.where(rng.random(63) < 0.5, -1, 1).astype(np.float32)
+        w = (tk * sign * c).astype(np.float32)
+        W[b, 0] = c if b % 2 else -c
+        W[b, 1:] = np.clip(w, -c, c)
+    W[10, 5] = np.float32(1e-40)       # denormal
+    W[11, 1:] = np.float32(3e-39)
+    W[12, :] = np.float32(1e-38)
+    W[13, 1:] = W[13, 1:] * np.float32(1e-30)
+    W = W.reshape(256, -1)
+    say("threshold boundary quantize")
+    q = Q.quantize_nf4_dq(torch.from_numpy(W).to("cuda"))
+    torch.cuda.synchronize()
+    check_quantizer(q, O.quantize_nf4_dq(W))
+
+
+# ------------------------------------------------------------------ full size
+
+def oracle_rows_for(W, rows):
+    """W'[rows] from the oracle's own quantization of the whole weight."""
+    m, n = W.shape
+    qw = O.quantize_nf4_dq(W)
+    return qw, O.dequant_rows(qw, m, n, rows)
+
+
+def full_layer_case(Q, cfg, layer, need_bwd):
+    L = layer
+    say(f"config{cfg} {L.name} {L.m}x{L.n} M={L.M} r={L.r}: drawing inputs")
+    inp = QI.layer_inputs(cfg, L, tensors=("W", "x", "g", "A", "B") if need_bwd else ("W", "x", "A", "B"))
+    W = inp["W"]
+    say(f"config{cfg} {L.name}: gpu quantize/fwd/bwd")
+    got = run_gpu(Q, W, inp["x"], inp.get("g"), inp["A"], inp["B"], L.s, need_bwd)
+    say(f"config{cfg} {L.name}: oracle quantize")
+    qw = O.quantize_nf4_dq(W)
+    check_quantizer(got["q"], qw)
+    rows = sample_indices(L.m, 96, 1000 * cfg + L.index)
+    toks = sample_indices(L.M, 48, 2000 * cfg + L.index)
+    cols = sample_indices(L.n, 96, 3000 * cfg + L.index)
+    Wr = O.dequant_rows(qw, L.m, L.n, rows)
+    deq = Q.dequant_nf4_dq(got["q"])
+    deq_rows = host_bits(deq[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(f64(deq_rows), Wr), "dequantized rows differ"
+    del deq
+    x = f64(inp["x"])
+    A = f64(inp["A"])
+    B = f64(inp["B"])
+    u_t = x[toks] @ A.T
+    h_ref = x[toks] @ Wr.T + L.s * (u_t @ B[rows].T)
+    h_got = f64(host_bits(got["h"][torch.from_numpy(toks).cuda()][:, torch.from_numpy(rows).cuda()]))
+    assert_close(h_got, h_ref, f"config{cfg} {L.name} h (sampled)")
+    assert_close(got["u"][torch.from_numpy(toks).cuda()].cpu().numpy(), u_t, f"config{cfg} {L.name} u (sampled)")
+    if not need_bwd:
+        return
+    say(f"config{cfg} {L.name}: oracle backward on samples")
+    g = f64(inp["g"])
+    Wc = O.dequant_cols(qw, L.m, L.n, cols)
+    v = g @ B
+    u = x @ A.T
+    gx_ref = g[toks] @ Wc + L.s * (v[toks] @ A[:, cols])
+    gA_ref = L.s * (v.T @ x[:, cols])
+    gB_ref = L.s * (g[:, rows].T @ u)
+    tc, cc, rc = (torch.from_numpy(a).cuda() for a in (toks, cols, rows))
+    assert_close(f64(host_bits(got["grad_x"][tc][:, cc])), gx_ref, f"config{cfg} {L.name} grad_x (sampled)")
+    assert_close(f64(host_bits(got["grad_A"][:, cc])), gA_ref, f"config{cfg} {L.name} grad_A (sampled)")
+    assert_close(f64(host_bits(got["grad_B"][rc])), gB_ref, f"config{cfg} {L.name} grad_B (sampled)")
+
+
+FULL = [(2, L) for L in QI.CONFIGS[2]["layers"]] + [(3, L) for L in QI.CONFIGS[3]["layers"]] \
+    + [(4, L) for L in QI.CONFIGS[4]["layers"]] + [(5, L) for L in QI.CONFIGS[5]["layers"]]
+
+
+@pytest.mark.parametrize("cfg,layer", FULL, ids=[f"cfg{c}-{L.name}" for c, L in FULL])
+def test_full_size_layer(Q, cfg, layer):
+    full_layer_case(Q, cfg, layer, need_bwd=QI.CONFIGS[cfg]["backward"])
+    torch.cuda.empty_cache()

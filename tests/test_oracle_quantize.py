@@ -223,3 +223,13 @@ def test_eq4_ratio(pages):
     approx = ex["r"] / min(ex["m"], ex["n"])
     assert approx * 100 < ex["printed_bound_percent"]      # the printed approximation
     assert abs(exact - 2 * approx) < 1e-15                 # square layers: exactly twice that
+
+
+def test_dequant_cols_matches_whole():
+    rng = np.random.default_rng(16)
+    m, n = 40, 16384 // 4 + 64
+    W = (rng.standard_normal((m, n)) * 0.02).astype(np.float32)
+    qw = O.quantize_nf4_dq(W)
+    full = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size)).reshape(m, n)
+    cols = [0, 1, 63, 64, 4095, n - 1, 777]
+    assert np.array_equal(O.dequant_cols(qw, m, n, cols), full[:, cols])
