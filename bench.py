@@ -1,0 +1,202 @@
+"""Benchmark of the QLoRA adapted-linear hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, already
+resident in HBM: quantize the frozen weight (NF4 + double quantization),
+forward (u = x A^T, h = x W'^T + s u B^T), backward (grad_x, grad_A,
+grad_B).  Workload: the Llama-3.1-8B-shaped gate projection, W0 14336 x
+4096, 4096 tokens (batch 4 x seq 1024), LoRA r = 16, alpha = 32.
+
+value = algorithmic forward + backward flops per step / step time (TFLOP/s),
+the quantizer's time included in the step.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def fwd_flops(M, n, m, r):
+    return 2 * M * m * n + 2 * M * r * (m + n)
+
+
+def bwd_flops(M, n, m, r):
+    return 2 * M * m * n + 4 * M * r * (m + n)
+
+
+def quant_bytes(m, n):
+    numel = m * n
+    return 4 * numel + numel // 2 + numel // 64 + 4 * ((numel // 64 + 255) // 256)
+
+
+def cpu_baseline(cfg, layer, tokens):
+    """Time the oracle (float64 numpy) on a bounded sample of the workload."""
+    import numpy as np
+
+    import qlora_inputs as QI
+    from oracle import qlora_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    L = layer
+    inp = QI.layer_inputs(cfg, L, M=tokens)
+    t0 = time.perf_counter()
+    qw = O.quantize_nf4_dq(inp["W"])
+    Wd = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], L.m * L.n)).reshape(L.m, L.n)
+    x = O.bf16_bits_to_float64(inp["x"])
+    g = O.bf16_bits_to_float64(inp["g"])
+    A = O.bf16_bits_to_float64(inp["A"])
+    B = O.bf16_bits_to_float64(inp["B"])
+    h, u = O.linear_fwd(x, Wd, A, B, L.s)
+    O.linear_bwd(x, g, Wd, A, B, L.s, u=u)
+    dt = time.perf_counter() - t0
+    flops = fwd_flops(tokens, L.n, L.m, L.r) + bwd_flops(tokens, L.n, L.m, L.r)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"quantize the full {L.m}x{L.n} weight + fwd + bwd for {tokens} of the {L.M} tokens, "
+                   f"float64 numpy; {dt:.2f} s; value = sample fwd+bwd flops / time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_fine_qlora_amd as Q
+    import qlora_inputs as QI
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+
+    cfg = 2
+    L = QI.CONFIGS[cfg]["layers"][0]
+    M, n, m, r, s = L.M, L.n, L.m, L.r, L.s
+    inp = QI.layer_inputs(cfg, L)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    W = torch.from_numpy(inp["W"]).to(dev)
+    x, g, A, B = (dev_bf16(inp[k]) for k in ("x", "g", "A", "B"))
+    q = Q.alloc_quantized(m, n, dev)
+    h = torch.empty((M, m), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((M, r), dtype=torch.float32, device=dev)
+    gx = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+    gA = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
+    gB = torch.empty((m, r), dtype=torch.bfloat16, device=dev)
+    ws_f = torch.empty(Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(Q.workspace_bytes(Q.QLORA_OP_BWD, M, n, m, r), dtype=torch.uint8, device=dev)
+
+    def step():
+        Q.quantize_nf4_dq(W, out=q)
+        Q.linear_fwd(x, q, A, B, s, h=h, u=u, workspace=ws_f)
+        Q.linear_bwd(x, g, q, A, B, s, u=u, out=(gx, gA, gB), workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    Q.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    Q.profile_enable(False)
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    flops = fwd_flops(M, n, m, r) + bwd_flops(M, n, m, r)
+    value = flops / (ms * 1e-3) / 1e12
+
+    kern = {}
+    for name in ("quantize", "fwd_gemm", "dgrad_gemm", "skinny_nt", "lora_grad", "reduce", "transpose"):
+        cnt, tot = Q.profile_query(name)
+        if cnt:
+            kern[name] = {"launches": cnt, "avg_us": tot * 1e3 / cnt}
+
+    per_launch = {
+        "fwd_gemm": 2 * M * m * n + 2 * M * m * r,
+        "dgrad_gemm": 2 * M * n * m + 2 * M * n * r,
+    }
+    dom = max(per_launch, key=lambda k: kern.get(k, {}).get("avg_us", 0.0))
+    dom_us = kern[dom]["avg_us"]
+    achieved = per_launch[dom] / (dom_us * 1e-6) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    qb = quant_bytes(m, n)
+    quant = {"avg_us": round(kern["quantize"]["avg_us"], 2),
+             "GB/s": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9, 1),
+             "hbm_frac": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    other = {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()}
+
+    out = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s and NF4 weight GB/s (% of roofline), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gate projection W0 14336x4096 NF4+DQ, 4096 tokens, r=16, alpha=32: "
+                               "quantize + fwd + bwd per step",
+                   "M": M, "n": n, "m": m, "r": r, "s": s},
+        "roofline": roofline,
+        "quantize": quant,
+        "kernels": other,
+    }
+    if not args.no_cpu_baseline:
+        del W, x, g, A, B, h, gx, ws_f, ws_b
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
