@@ -121,7 +121,8 @@ qlora_status check_linear(int64_t M, int64_t n, int64_t m, int32_t r, float s) {
   qlora_status st = check_weight_shape(m, n);
   if (st != QLORA_OK) return st;
   if (M <= 0 || M >= kMaxDim) return QLORA_ERR_SHAPE;
-  if (M > ((int64_t)1 << 40) / (n > m ? n : m)) return QLORA_ERR_SHAPE;
+  // activation element offsets are 32-bit inside the GEMM kernels
+  if (M > (((int64_t)1 << 31) - 1) / (n > m ? n : m)) return QLORA_ERR_SHAPE;
   if (r < 1 || r > kMaxRank) return QLORA_ERR_RANK;
   if (!std::isfinite(s)) return QLORA_ERR_VALUE;
   return QLORA_OK;

@@ -132,6 +132,51 @@ __device__ __forceinline__ void lut_dequant8(const BlockLut& L, uint32_t w, uint
   out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u);
 }
 
+
+// Magnitude table of one block for the sign-symmetric NF4 levels: entry j
+// (0..7) is bf16(fl32(Q[8+j] * s)); Q[c] = -Q[15-c] exactly, so the code c
+// dequantizes to entry (c >= 8 ? c - 8 : 7 - c) with the sign bit set for
+// c < 8 (which also gives -0.0 for a zero scale, as bf16(fl32(Q[c] * 0))).
+// lo[k] / hi[k] hold the low / high bytes of entries 4k..4k+3.
+struct MagLut {
+  uint32_t lo[2];
+  uint32_t hi[2];
+};
+
+__device__ __forceinline__ MagLut make_mag_lut(const Nf4Table& tab, float s) {
+  uint32_t pr[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pr[k] = pack_bf16x2(tab.q[8 + 2 * k] * s, tab.q[9 + 2 * k] * s);
+  MagLut L;
+  L.lo[0] = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
+  L.hi[0] = __builtin_amdgcn_perm(pr[1], pr[0], 0x07050301u);
+  L.lo[1] = __builtin_amdgcn_perm(pr[3], pr[2], 0x06040200u);
+  L.hi[1] = __builtin_amdgcn_perm(pr[3], pr[2], 0x07050301u);
+  return L;
+}
+
+// Same contract as lut_dequant8, using the magnitude table: 24 VALU ops for
+// 8 weights.
+__device__ __forceinline__ void mag_dequant8(const MagLut& L, uint32_t w, uint32_t out[4]) {
+  const uint32_t nw = ~w;
+  const uint32_t t = (nw >> 3) & 0x11111111u;   // 1 in each nibble whose code is < 8
+  const uint32_t X = w ^ ((t << 3) - t);         // low 3 bits of each nibble: table index
+  const uint32_t sel_e = X & 0x07070707u;        // even elements (low nibbles)
+  const uint32_t sel_o = (X >> 4) & 0x07070707u; // odd elements (high nibbles)
+  const uint32_t LE = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_e);
+  const uint32_t LO = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_o);
+  const uint32_t HE = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_e) | ((nw << 4) & 0x80808080u);
+  const uint32_t HO = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_o) | (nw & 0x80808080u);
+  const uint32_t l03 = __builtin_amdgcn_perm(LO, LE, 0x05010400u);
+  const uint32_t l47 = __builtin_amdgcn_perm(LO, LE, 0x07030602u);
+  const uint32_t h03 = __builtin_amdgcn_perm(HO, HE, 0x05010400u);
+  const uint32_t h47 = __builtin_amdgcn_perm(HO, HE, 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(h03, l03, 0x05010400u);
+  out[1] = __builtin_amdgcn_perm(h03, l03, 0x07030602u);
+  out[2] = __builtin_amdgcn_perm(h47, l47, 0x05010400u);
+  out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);

@@ -117,9 +117,9 @@ __global__ __launch_bounds__(256) void dequant_nf4_dq_kernel(const uint32_t* __r
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nwords) return;
   const int64_t blk = i >> 3;  // 8 words of codes per 64-weight block
-  const BlockLut L = make_block_lut(tab, block_scale(absmax8, c2, blk));
+  const MagLut L = make_mag_lut(tab, block_scale(absmax8, c2, blk));
   uint32_t o[4];
-  lut_dequant8(L, codes[i], o);
+  mag_dequant8(L, codes[i], o);
   out[i] = u32x4{o[0], o[1], o[2], o[3]};
 }
 
