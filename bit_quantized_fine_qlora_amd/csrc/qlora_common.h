@@ -3,7 +3,8 @@
 // Data layout (row-major everywhere):
 //   W0      m x n fp32 (out x in); quantized in 64-element blocks that run
 //           along n, 256 blocks (16384 elements) per double-quant group.
-//   codes   m*n/2 bytes, element 2k in the low nibble of byte k.
+//   codes   m*n/2 bytes: sign-magnitude 4-bit codes (see MagLut), per 8
+//           weights byte j = weight j (low nibble) | weight j+4 (high nibble).
 //   absmax8 m*n/64 bytes, E4M3FN code of c1_b / c2_g.
 //   c2      ceil(m*n/16384) fp32.
 //   x M x n, g M x m, A r x n, B m x r, h M x m, grad_x M x n: bf16 bits.
@@ -76,68 +77,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// 16-entry bf16 lookup table for one block, held as byte planes so that
-// v_perm_b32 can look up four entries at once:
-//   lo[k] holds the low bytes of entries 4k..4k+3, hi[k] their high bytes.
-struct BlockLut {
-  uint32_t lo[4];
-  uint32_t hi[4];
-};
-
-// Build the table of W' = bf16(fl32(Q[c] * s)) for c = 0..15.
-__device__ __forceinline__ BlockLut make_block_lut(const Nf4Table& tab, float s) {
-  uint32_t pr[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) pr[k] = pack_bf16x2(tab.q[2 * k] * s, tab.q[2 * k + 1] * s);
-  BlockLut L;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // pr[2k] = (e0 | e1 << 16), pr[2k+1] = (e2 | e3 << 16)
-    L.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
-    L.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
-  }
-  return L;
-}
-
-// Dequantize the 8 codes of one 32-bit word (elements e0..e7, e0 in the low
-// nibble) into 4 words of bf16 pairs (e0,e1) (e2,e3) (e4,e5) (e6,e7).
-__device__ __forceinline__ void lut_dequant8(const BlockLut& L, uint32_t w, uint32_t out[4]) {
-  const uint32_t sel_e = w & 0x07070707u;          // even elements: low nibble of each byte
-  const uint32_t sel_o = (w >> 4) & 0x07070707u;   // odd elements: high nibble
-  // byte masks 0xFF where the code is >= 8 (bit 3 of the nibble)
-  const uint32_t te = (w >> 3) & 0x01010101u;
-  const uint32_t to = (w >> 7) & 0x01010101u;
-  const uint32_t me = (te << 8) - te;
-  const uint32_t mo = (to << 8) - to;
-  const uint32_t lo_e = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_e);
-  const uint32_t lo_e8 = __builtin_amdgcn_perm(L.lo[3], L.lo[2], sel_e);
-  const uint32_t hi_e = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_e);
-  const uint32_t hi_e8 = __builtin_amdgcn_perm(L.hi[3], L.hi[2], sel_e);
-  const uint32_t lo_o = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_o);
-  const uint32_t lo_o8 = __builtin_amdgcn_perm(L.lo[3], L.lo[2], sel_o);
-  const uint32_t hi_o = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_o);
-  const uint32_t hi_o8 = __builtin_amdgcn_perm(L.hi[3], L.hi[2], sel_o);
-  const uint32_t LE = (lo_e8 & me) | (lo_e & ~me);  // v_bfi_b32
-  const uint32_t HE = (hi_e8 & me) | (hi_e & ~me);
-  const uint32_t LO = (lo_o8 & mo) | (lo_o & ~mo);
-  const uint32_t HO = (hi_o8 & mo) | (hi_o & ~mo);
-  // low bytes of e0 e1 e2 e3 and of e4 e5 e6 e7, then the high bytes
-  const uint32_t l03 = __builtin_amdgcn_perm(LO, LE, 0x05010400u);
-  const uint32_t l47 = __builtin_amdgcn_perm(LO, LE, 0x07030602u);
-  const uint32_t h03 = __builtin_amdgcn_perm(HO, HE, 0x05010400u);
-  const uint32_t h47 = __builtin_amdgcn_perm(HO, HE, 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(h03, l03, 0x05010400u);
-  out[1] = __builtin_amdgcn_perm(h03, l03, 0x07030602u);
-  out[2] = __builtin_amdgcn_perm(h47, l47, 0x05010400u);
-  out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u);
-}
-
-
-// Magnitude table of one block for the sign-symmetric NF4 levels: entry j
-// (0..7) is bf16(fl32(Q[8+j] * s)); Q[c] = -Q[15-c] exactly, so the code c
-// dequantizes to entry (c >= 8 ? c - 8 : 7 - c) with the sign bit set for
-// c < 8 (which also gives -0.0 for a zero scale, as bf16(fl32(Q[c] * 0))).
-// lo[k] / hi[k] hold the low / high bytes of entries 4k..4k+3.
+// Stored 4-bit code of an NF4 level L (0..15): bit 3 = sign (set for the 8
+// negative levels), bits 0-2 = rank of |level| among the 8 positive levels
+// (code = L - 8 for L >= 8, 15 - L for L < 8; the levels are symmetric).  In
+// each 32-bit word of codes (8 consecutive weights), byte j holds weight j
+// in its low nibble and weight j + 4 in its high nibble.
+//
+// Magnitude table of one block: entry k (0..7) is bf16(fl32(Q[8+k] * s)).
+// Since Q[15-k'] = -Q[k'] exactly and both roundings are sign-symmetric, a
+// weight dequantizes to its entry with the code's sign bit copied into the
+// bf16 sign (which also gives -0.0 for a zero scale, as bf16(fl32(Q * 0))
+// does for a negative level).  lo[i] / hi[i] hold the low / high bytes of
+// entries 4i..4i+3.
 struct MagLut {
   uint32_t lo[2];
   uint32_t hi[2];
@@ -155,26 +106,19 @@ __device__ __forceinline__ MagLut make_mag_lut(const Nf4Table& tab, float s) {
   return L;
 }
 
-// Same contract as lut_dequant8, using the magnitude table: 24 VALU ops for
-// 8 weights.
+// Dequantize one 32-bit word of codes (8 weights) into 4 words of bf16
+// pairs in weight order (w0,w1) (w2,w3) (w4,w5) (w6,w7): 14 VALU ops.
 __device__ __forceinline__ void mag_dequant8(const MagLut& L, uint32_t w, uint32_t out[4]) {
-  const uint32_t nw = ~w;
-  const uint32_t t = (nw >> 3) & 0x11111111u;   // 1 in each nibble whose code is < 8
-  const uint32_t X = w ^ ((t << 3) - t);         // low 3 bits of each nibble: table index
-  const uint32_t sel_e = X & 0x07070707u;        // even elements (low nibbles)
-  const uint32_t sel_o = (X >> 4) & 0x07070707u; // odd elements (high nibbles)
-  const uint32_t LE = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_e);
-  const uint32_t LO = __builtin_amdgcn_perm(L.lo[1], L.lo[0], sel_o);
-  const uint32_t HE = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_e) | ((nw << 4) & 0x80808080u);
-  const uint32_t HO = __builtin_amdgcn_perm(L.hi[1], L.hi[0], sel_o) | (nw & 0x80808080u);
-  const uint32_t l03 = __builtin_amdgcn_perm(LO, LE, 0x05010400u);
-  const uint32_t l47 = __builtin_amdgcn_perm(LO, LE, 0x07030602u);
-  const uint32_t h03 = __builtin_amdgcn_perm(HO, HE, 0x05010400u);
-  const uint32_t h47 = __builtin_amdgcn_perm(HO, HE, 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(h03, l03, 0x05010400u);
-  out[1] = __builtin_amdgcn_perm(h03, l03, 0x07030602u);
-  out[2] = __builtin_amdgcn_perm(h47, l47, 0x05010400u);
-  out[3] = __builtin_amdgcn_perm(h47, l47, 0x07030602u);
+  const uint32_t s03 = w & 0x07070707u;          // ranks of weights 0..3 (low nibbles)
+  const uint32_t s47 = (w >> 4) & 0x07070707u;   // ranks of weights 4..7 (high nibbles)
+  const uint32_t L03 = __builtin_amdgcn_perm(L.lo[1], L.lo[0], s03);
+  const uint32_t L47 = __builtin_amdgcn_perm(L.lo[1], L.lo[0], s47);
+  const uint32_t H03 = __builtin_amdgcn_perm(L.hi[1], L.hi[0], s03) | ((w << 4) & 0x80808080u);
+  const uint32_t H47 = __builtin_amdgcn_perm(L.hi[1], L.hi[0], s47) | (w & 0x80808080u);
+  out[0] = __builtin_amdgcn_perm(H03, L03, 0x05010400u);
+  out[1] = __builtin_amdgcn_perm(H03, L03, 0x07030602u);
+  out[2] = __builtin_amdgcn_perm(H47, L47, 0x05010400u);
+  out[3] = __builtin_amdgcn_perm(H47, L47, 0x07030602u);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {

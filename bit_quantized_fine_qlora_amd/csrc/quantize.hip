@@ -22,12 +22,21 @@ __device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) 
   return __builtin_fmaf(r1, y, q1);
 }
 
-// Code = number of thresholds strictly below the normalized weight.
-__device__ __forceinline__ uint32_t nf4_code(float v, const Nf4Table& tab) {
-  uint32_t c = 0;
+// Stored code of the level nearest to v: the level index is the number of
+// thresholds strictly below v.  With the symmetric table this is computed on
+// |v| against the 7 positive thresholds, as integers (bit patterns of
+// non-negative floats order like the floats):
+//   v > 0 : level 8 + #{T_j < v}        -> code #{T_j < |v|}
+//   v <= 0: level 7 - #{T_j <= |v|}     -> code 8 + #{T_j < succ(|v|)}
+// (succ(|v|) is |v|'s bit pattern + 1; -0 and +0 both give level 7).
+__device__ __forceinline__ uint32_t nf4_code(float v, const uint32_t (&tb)[7]) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t neg = ((int32_t)bits <= 0) ? 1u : 0u;
+  const uint32_t key = (bits & 0x7FFFFFFFu) + neg;
+  uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < 15; ++j) c += (v > tab.t[j]) ? 1u : 0u;
-  return c;
+  for (int j = 0; j < 7; ++j) m += (key > tb[j]) ? 1u : 0u;
+  return m | (neg << 3);
 }
 
 // One workgroup per double-quant group (256 blocks of 64 weights).  In each
@@ -42,6 +51,9 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   const int tid = threadIdx.x;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
   const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
+  uint32_t tb[7];  // bit patterns of the positive thresholds T_8..T_14
+#pragma unroll
+  for (int j = 0; j < 7; ++j) tb[j] = __float_as_uint(tab.t[8 + j]);
 
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
@@ -82,11 +94,13 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
 #pragma unroll
       for (int i = 0; i < 16; ++i) q[i] = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
     }
+    // pack: per 8 weights, byte j = code(w_j) | code(w_{j+4}) << 4
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= nf4_code(q[i], tab) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= nf4_code(q[8 + i], tab) << (4 * i);
+    for (int j = 0; j < 4; ++j) {
+      lo |= (nf4_code(q[j], tb) | (nf4_code(q[j + 4], tb) << 4)) << (8 * j);
+      hi |= (nf4_code(q[8 + j], tb) | (nf4_code(q[12 + j], tb) << 4)) << (8 * j);
+    }
     if (valid) {
       u32x2 pk = {lo, hi};
       *reinterpret_cast<u32x2*>(codes + (blk0 + lb) * (kBlock / 2) + quarter * 8) = pk;

@@ -38,8 +38,12 @@ its reason, in the design notes of the repository):
   * blocks are 64 consecutive elements of the row-major (out x in) weight
   * the 8-bit float is OCP E4M3FN, round to nearest, ties to even
   * c2 is the plain fp32 max of the 256 c1 values of its group
-  * an all-zero block has c1 = 0, every normalized weight is 0 (code 7)
-  * the code of element 2k sits in the low nibble of byte k
+  * an all-zero block has c1 = 0, every normalized weight is 0 (level 7)
+  * a level L (0..15, ascending) is stored as a 4-bit code with the sign in
+    bit 3 and the magnitude rank in bits 0-2: code = L - 8 for L >= 8 and
+    15 - L for L < 8; in every group of 8 consecutive weights, byte j of the
+    group's 4 bytes holds weight j in its low nibble and weight j + 4 in its
+    high nibble
   * s = alpha / r multiplies every adapter term, gradients included
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
@@ -187,8 +191,9 @@ def quantize_nf4_dq(W) -> dict:
     Steps, in the pages' order:
       1. c1_b = max |w| over block b (64 consecutive weights)      [P1] Eq. 1
       2. w_hat = fl32(w / c1_b) (alpha = 1); an all-zero block gives 0
-      3. code = number of thresholds T_j strictly below w_hat      [P1] Step 1
-      4. byte k holds the codes of elements 2k (low) and 2k+1 (high)
+      3. level = number of thresholds T_j strictly below w_hat     [P1] Step 1
+      4. levels written as sign-magnitude 4-bit codes, packed per group of 8
+         weights (see pack_levels)
       5. c2_g = max c1 over group g of 256 blocks                   [P1] Step 2
       6. a_b = E4M3(fl32(c1_b / c2_g)); a zero group gives a_b = 0  [P4] Innov. 2
     The element count must be a multiple of 64; the last group may hold
@@ -207,11 +212,10 @@ def quantize_nf4_dq(W) -> dict:
     safe = np.where(c1 > 0, c1, np.float32(1.0)).astype(np.float32)
     w_hat = (wb / safe[:, None]).astype(np.float32)                         # step 2
     w_hat = np.where(c1[:, None] > 0, w_hat, np.float32(0.0))
-    codes = np.zeros(wb.shape, dtype=np.uint8)
+    level = np.zeros(wb.shape, dtype=np.uint8)
     for t in NF4_T:                                                         # step 3
-        codes += (w_hat > t).astype(np.uint8)
-    flat = codes.reshape(-1)
-    packed = (flat[0::2] | (flat[1::2] << 4)).astype(np.uint8)              # step 4
+        level += (w_hat > t).astype(np.uint8)
+    packed = pack_levels(level.reshape(-1))                                 # step 4
     ngrp = (nblk + DQ_BLOCKS - 1) // DQ_BLOCKS
     c2 = np.zeros(ngrp, dtype=np.float32)
     for g in range(ngrp):                                                   # step 5
@@ -224,13 +228,39 @@ def quantize_nf4_dq(W) -> dict:
     return dict(codes=packed, absmax8=absmax8, c2=c2, c1=c1)
 
 
+def level_to_code(level) -> np.ndarray:
+    """4-bit code of an NF4 level: sign in bit 3, magnitude rank in bits 0-2.
+
+    The 16 levels are symmetric (level 15 - L is minus level L), so a level is
+    written as its sign (bit 3 set for the 8 negative levels) and the rank of
+    its magnitude among the 8 positive levels: code = L - 8 for L >= 8 and
+    15 - L for L < 8.  The pages fix the levels, not their bit patterns.
+    """
+    L = np.asarray(level, dtype=np.int64)
+    return np.where(L >= 8, L - 8, 15 - L).astype(np.uint8)
+
+
+def code_to_level(code) -> np.ndarray:
+    c = np.asarray(code, dtype=np.int64)
+    return np.where(c < 8, c + 8, 15 - c).astype(np.uint8)
+
+
+def pack_levels(level) -> np.ndarray:
+    """Pack levels (numel a multiple of 8) into bytes.
+
+    In each group of 8 consecutive weights, byte j (j = 0..3) of the group's
+    4 bytes holds the code of weight j in its low nibble and of weight j + 4
+    in its high nibble.
+    """
+    c = level_to_code(level).reshape(-1, 8)
+    return (c[:, 0:4] | (c[:, 4:8] << 4)).astype(np.uint8).reshape(-1)
+
+
 def unpack_codes(codes, numel: int) -> np.ndarray:
-    """Nibble codes of each element, element 2k from the low nibble of byte k."""
-    codes = np.asarray(codes, dtype=np.uint8)
-    out = np.empty(numel, dtype=np.uint8)
-    out[0::2] = codes[: numel // 2] & 0xF
-    out[1::2] = codes[: numel // 2] >> 4
-    return out
+    """NF4 level (0..15) of each element; inverse of pack_levels."""
+    b = np.asarray(codes, dtype=np.uint8)[: numel // 2].reshape(-1, 4)
+    c = np.concatenate([b & 0xF, b >> 4], axis=1).reshape(-1)
+    return code_to_level(c)
 
 
 def block_scales(absmax8, c2, nblk: int) -> np.ndarray:
@@ -264,8 +294,8 @@ def dequant_cols(qw: dict, m: int, n: int, cols) -> np.ndarray:
     """float64 values of W'[:, cols] for an m x n weight (same definition)."""
     cols = np.asarray(cols, dtype=np.int64)
     e = (np.arange(m, dtype=np.int64)[:, None] * n + cols[None, :]).reshape(-1)
-    byte = np.asarray(qw["codes"], dtype=np.uint8)[e // 2]
-    code = np.where(e % 2 == 0, byte & 0xF, byte >> 4)
+    byte = np.asarray(qw["codes"], dtype=np.uint8)[(e // 8) * 4 + (e % 4)]
+    code = code_to_level(np.where((e % 8) < 4, byte & 0xF, byte >> 4))
     blk = e // BLOCK
     dec = e4m3_decode(np.asarray(qw["absmax8"])[blk]).astype(np.float32)
     s = (dec * np.asarray(qw["c2"], dtype=np.float32)[blk // DQ_BLOCKS]).astype(np.float32)

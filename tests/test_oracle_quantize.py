@@ -233,3 +233,30 @@ def test_dequant_cols_matches_whole():
     full = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size)).reshape(m, n)
     cols = [0, 1, 63, 64, 4095, n - 1, 777]
     assert np.array_equal(O.dequant_cols(qw, m, n, cols), full[:, cols])
+
+
+def test_code_encoding_is_sign_and_magnitude():
+    # every stored code denotes its level: sign in bit 3, magnitude rank in bits 0-2
+    L = np.arange(16)
+    c = O.level_to_code(L)
+    assert sorted(c.tolist()) == list(range(16))                 # a bijection
+    assert np.array_equal(O.code_to_level(c), L)
+    for lev, code in zip(L, c):
+        mag = O.NF4_Q[8 + (code & 7)]
+        val = O.NF4_Q[lev]
+        assert (code >> 3) == (1 if val < 0 else 0)
+        assert float(abs(val)) == float(mag)
+
+
+def test_packing_order_and_roundtrip():
+    rng = np.random.default_rng(17)
+    lev = rng.integers(0, 16, size=64 * 5).astype(np.uint8)
+    packed = O.pack_levels(lev)
+    assert packed.size == lev.size // 2
+    assert np.array_equal(O.unpack_codes(packed, lev.size), lev)
+    # byte j of each 8-weight group: weight j low nibble, weight j + 4 high nibble
+    codes = O.level_to_code(lev)
+    for g in range(lev.size // 8):
+        for j in range(4):
+            b = int(packed[4 * g + j])
+            assert b & 0xF == codes[8 * g + j] and b >> 4 == codes[8 * g + j + 4]
