@@ -20,8 +20,8 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
                      float s, const Nf4Table& tab, hipStream_t stream);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
-                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m, int r,
-                       float s, const Nf4Table& tab, hipStream_t stream);
+                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
+                       int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream);
 int skinny_splits(int64_t M, int64_t K);
 int64_t skinny_kc(int64_t K, int splits);
 void launch_skinny_nt(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
@@ -31,6 +31,8 @@ int64_t grad_tc(int64_t M, int splits);
 void launch_lora_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, float s, int splits,
                       float* part, int transpose_out, uint16_t* out, hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t stream);
+void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
+                          hipStream_t stream);
 
 namespace {
 
@@ -121,8 +123,10 @@ qlora_status check_linear(int64_t M, int64_t n, int64_t m, int32_t r, float s) {
   qlora_status st = check_weight_shape(m, n);
   if (st != QLORA_OK) return st;
   if (M <= 0 || M >= kMaxDim) return QLORA_ERR_SHAPE;
-  // activation element offsets are 32-bit inside the GEMM kernels
-  if (M > (((int64_t)1 << 31) - 1) / (n > m ? n : m)) return QLORA_ERR_SHAPE;
+  // the GEMM kernels address activations and the packed weight with 32-bit
+  // byte offsets: M*max(n,m) < 2^30 and m*n < 2^31
+  if (M >= ((int64_t)1 << 30) / (n > m ? n : m)) return QLORA_ERR_SHAPE;
+  if (m >= ((int64_t)1 << 31) / n) return QLORA_ERR_SHAPE;
   if (r < 1 || r > kMaxRank) return QLORA_ERR_RANK;
   if (!std::isfinite(s)) return QLORA_ERR_VALUE;
   return QLORA_OK;
@@ -159,8 +163,9 @@ FwdWs fwd_ws(int64_t M, int64_t n, int32_t r) {
 }
 
 struct BwdWs {
-  size_t At, Bt, part_uv, u, v, gA, gB, total;
+  size_t At, Bt, part_uv, u, v, gA, gB, gpad, total;
   int su, sv, sa, sb;
+  int64_t m_pad;  // g's row length as the input-gradient GEMM reads it
 };
 
 BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
@@ -178,6 +183,11 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   w.v = L.take((size_t)M * r * sizeof(float));
   w.gA = L.take((size_t)w.sa * n * r * sizeof(float));
   w.gB = L.take((size_t)w.sb * m * r * sizeof(float));
+  // The input-gradient GEMM reads g in 16-byte chunks with a per-dword range
+  // check; rows whose length is not a multiple of 8 are first copied into a
+  // zero-padded buffer of row length m rounded up to 64.
+  w.m_pad = (m % 8 == 0) ? m : ((m + 63) / 64) * 64;
+  w.gpad = (m % 8 == 0) ? 0 : L.take((size_t)M * w.m_pad * 2);
   w.total = L.total;
   return w;
 }
@@ -324,8 +334,15 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
       Timed tm("transpose", hs);
       launch_transpose_bf16(A, r, n, At, hs);
     }
+    const uint16_t* gk = g;
+    if (w.m_pad != m) {
+      Timed tp("transpose", hs);
+      uint16_t* gp = at<uint16_t>(workspace, w.gpad);
+      launch_pad_cols_bf16(g, M, m, w.m_pad, gp, hs);
+      gk = gp;
+    }
     Timed tm("dgrad_gemm", hs);
-    launch_dgrad_gemm(g, codes, absmax8, c2, At, v, grad_x, M, n, m, r, s, table(), hs);
+    launch_dgrad_gemm(gk, codes, absmax8, c2, At, v, grad_x, M, n, m, w.m_pad, r, s, table(), hs);
   }
   return hip_status();
 }

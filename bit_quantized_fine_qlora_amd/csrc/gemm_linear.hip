@@ -49,6 +49,7 @@ struct GemmArgs {
   uint16_t* out;           // M x N
   int64_t M, K, N;         // tokens, contraction, output features
   int64_t wn;              // columns of W0 (n)
+  int64_t wm;              // rows of W0 (m)
   int r;
   float s;
   int tiles_f;
@@ -89,24 +90,34 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
   const int64_t t0 = (int64_t)tile_t * lg2::BT;
   const int64_t K = p.K;
   const int nk = (int)((K + lg2::BK - 1) / lg2::BK);
-  const int nk_full = (int)(K / lg2::BK);
   const int64_t wn = p.wn;
-  const bool dq_wave = wave < 4;
+  const int64_t wnumel = p.wm * wn;
   const int wf = (wave & 1) * 128;  // this wave's 128 output features in the tile
   const int wt = (wave >> 1) * 64;  // this wave's 64 tokens
 
+  // Buffer resources: reads past a tensor's end return 0.  Rows past M (or
+  // past m / n of W0) read zeros or other rows of the same tensor; they only
+  // feed outputs that are never stored.  In the backward's last K step the
+  // W0 rows past m read zero codes and a zero 8-bit constant, i.e. zero
+  // weights, so the finite activations there add nothing.
+  const brsrc_t r_act = make_rsrc(p.act, (uint32_t)(p.M * K * 2));
+  const brsrc_t r_codes = make_rsrc(p.codes, (uint32_t)(wnumel / 2));
+  const brsrc_t r_amax = make_rsrc(p.absmax8, (uint32_t)(wnumel / kBlock));
+  const brsrc_t r_c2 = make_rsrc(p.c2, (uint32_t)(((wnumel / kBlock + kGroupBlocks - 1) / kGroupBlocks) * 4));
+
   // ---- dequant assignment (threads 0..255): one 64-weight block per K step ----
-  // forward : LDS row tid = out feature f0 + tid; the block is (row, K step)
-  // backward: LDS row tid/4 = W0 row k0 + tid/4, features f0 + 64*(tid%4) .. +63
-  int64_t d_wrow, d_wcol;   // W0 element of the first weight at K step 0
+  // forward : LDS row tid = out feature f0 + tid, block (f0 + tid, ks)
+  // backward: LDS row tid/4 = W0 row 64*ks + tid/4, features f0 + 64*(tid%4) .. +63
+  const int dt = tid & 255;
+  uint32_t c_off, c_step, b_off, b_step;  // byte offsets of codes and absmax8 at step 0, per-step increments
   if (!kBwd) {
-    const int64_t f = f0 + (tid & 255);
-    d_wrow = f < p.N ? f : p.N - 1;     // clamped rows only feed unstored outputs
-    d_wcol = 0;
+    const int64_t e0 = (f0 + dt) * wn;
+    c_off = (uint32_t)(e0 / 2);  c_step = lg2::BK / 2;
+    b_off = (uint32_t)(e0 / kBlock);  b_step = 1;
   } else {
-    const int64_t j = f0 + 64 * (tid & 3);
-    d_wrow = (tid & 255) >> 2;
-    d_wcol = j < wn ? j : wn - 64;      // clamped blocks only feed unstored outputs
+    const int64_t e0 = (int64_t)(dt >> 2) * wn + f0 + 64 * (dt & 3);
+    c_off = (uint32_t)(e0 / 2);  c_step = (uint32_t)(lg2::BK * wn / 2);
+    b_off = (uint32_t)(e0 / kBlock);  b_step = (uint32_t)(lg2::BK * wn / kBlock);
   }
 
   // ---- activation tile loads: chunk id = i*512 + tid -> row id/8, chunk id%8 ----
@@ -114,11 +125,7 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
   const int a_c = tid & 7;
   uint32_t a_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int64_t t = t0 + 64 * i + a_row0;
-    t = t < p.M ? t : p.M - 1;          // clamped rows only feed unstored outputs
-    a_off[i] = (uint32_t)(t * K + 8 * a_c);
-  }
+  for (int i = 0; i < 4; ++i) a_off[i] = (uint32_t)(((t0 + 64 * i + a_row0) * K + 8 * a_c) * 2);
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -129,22 +136,13 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
   u32x4 areg[4];        // activation chunks of the next K step
   u32x4 creg[2];        // 64 codes of the next dequant step
   uint32_t aa = 0;      // absmax8 byte
-  float sa = 0.f;       // c2 of the group (0 for W0 rows past m)
+  float sa = 0.f;       // c2 of the group
 
-  auto load_act = [&](int ks) {
-    const int64_t k0 = (int64_t)ks * lg2::BK + 8 * a_c;
-    const bool partial = ks >= nk_full;  // only the last step of a backward with m % 64 != 0
+  auto load_act = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (!partial) {
-        areg[i] = *reinterpret_cast<const u32x4*>(p.act + (a_off[i] + (uint32_t)(ks * lg2::BK)));
-      } else {
-        const uint16_t* src = p.act + (a_off[i] - 8 * a_c);
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 8; ++e)
-          if (k0 + e < K) w[e >> 1] |= (uint32_t)src[k0 + e] << (16 * (e & 1));
-        areg[i] = u32x4{w[0], w[1], w[2], w[3]};
-      }
+      areg[i] = bload128(r_act, a_off[i]);
+      a_off[i] += lg2::BK * 2;
     }
   };
   auto store_act = [&](int stage) {
@@ -152,23 +150,13 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dA + sw64(64 * i + a_row0, a_c)) = areg[i];
   };
-  auto load_w = [&](int ks) {
-    int64_t wr = d_wrow, wc = d_wcol;
-    bool ok = true;
-    if (!kBwd) {
-      wc += (int64_t)ks * lg2::BK;
-    } else {
-      wr += (int64_t)ks * lg2::BK;
-      ok = wr < K;                  // rows of W0 past m act as zero weights
-      if (!ok) wr = K - 1;
-    }
-    const int64_t e0 = wr * wn + wc;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(p.codes + e0 / 2);
-    creg[0] = cp[0];
-    creg[1] = cp[1];
-    const int64_t blk = e0 / kBlock;
-    aa = p.absmax8[blk];
-    sa = ok ? p.c2[blk >> 8] : 0.0f;
+  auto load_w = [&]() {
+    creg[0] = bload128(r_codes, c_off);
+    creg[1] = bload128(r_codes, c_off + 16);
+    aa = bload8(r_amax, b_off);
+    sa = __uint_as_float(bload32(r_c2, (b_off >> 8) << 2));
+    c_off += c_step;
+    b_off += b_step;
   };
   auto dequant_store = [&](int stage) {
     uint8_t* dW = smem + stage * lg2::STAGEB;
@@ -177,11 +165,13 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
     for (int d = 0; d < 8; ++d) {
       uint32_t o[4];
       mag_dequant8(L, creg[d >> 2][d & 3], o);
-      const uint32_t off = kBwd ? swbwd((tid & 255) >> 2, 64 * (tid & 3) + 8 * d) : sw64(tid & 255, d);
+      const uint32_t off = kBwd ? swbwd(dt >> 2, 64 * (dt & 3) + 8 * d) : sw64(dt, d);
       *reinterpret_cast<u32x4*>(dW + off) = u32x4{o[0], o[1], o[2], o[3]};
     }
   };
-  auto mfma_step = [&](const uint8_t* sW, const uint8_t* sA, int kk) {
+  auto mfma_step = [&](int stage, int kk) {
+    const uint8_t* sW = smem + stage * lg2::STAGEB;
+    const uint8_t* sA = sW + lg2::WTILEB;
     u32x4 b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4*>(sA + sw64(wt + 16 * j + lr, 4 * kk + lq));
@@ -204,36 +194,44 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a, b[j], acc[i][j]);
     }
   };
+  // One K step on LDS stage `stage`: the registers holding step ks+1 go to
+  // the other stage (activations stored, W' dequantized by waves 0-3) while
+  // the MFMAs run, and the loads of step ks+2 are issued.
+  auto step_dq = [&](int stage) {
+    store_act(stage ^ 1);
+    load_act();
+    mfma_step(stage, 0);
+    dequant_store(stage ^ 1);
+    load_w();
+    mfma_step(stage, 1);
+    __syncthreads();
+  };
+  auto step_mm = [&](int stage) {
+    store_act(stage ^ 1);
+    load_act();
+    mfma_step(stage, 0);
+    mfma_step(stage, 1);
+    __syncthreads();
+  };
 
   // prologue: stage 0 <- step 0; registers <- step 1
-  load_act(0);
-  if (dq_wave) load_w(0);
+  const bool dq_wave = wave < 4;
+  load_act();
+  if (dq_wave) load_w();
   store_act(0);
   if (dq_wave) {
     dequant_store(0);
-    load_w(nk > 1 ? 1 : 0);
+    load_w();
   }
-  load_act(nk > 1 ? 1 : 0);
+  load_act();
   __syncthreads();
 
-  // Step ks: MFMAs on stage ks%2 while the registers holding step ks+1 go to
-  // the other stage (activations stored, W' dequantized) and the loads of
-  // step ks+2 are issued.
+  if (dq_wave) {
 #pragma unroll 1
-  for (int ks = 0; ks < nk; ++ks) {
-    const int stage = ks & 1;
-    const uint8_t* sW = smem + stage * lg2::STAGEB;
-    const uint8_t* sA = sW + lg2::WTILEB;
-    const int k2 = (ks + 2 < nk) ? ks + 2 : nk - 1;
-    store_act(stage ^ 1);
-    load_act(k2);
-    mfma_step(sW, sA, 0);
-    if (dq_wave) {
-      dequant_store(stage ^ 1);
-      load_w(k2);
-    }
-    mfma_step(sW, sA, 1);
-    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) step_dq(ks & 1);
+  } else {
+#pragma unroll 1
+    for (int ks = 0; ks < nk; ++ks) step_mm(ks & 1);
   }
 
   // ---- epilogue: + s * lora_b lora_a^T as extra K=32 MFMA steps (fp32 factor split hi + lo) ----
@@ -320,16 +318,18 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
                      float s, const Nf4Table& tab, hipStream_t stream) {
   GemmArgs p{};
   p.act = x; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = B; p.lora_b = u; p.out = h;
-  p.M = M; p.K = n; p.N = m; p.wn = n; p.r = r; p.s = s;
+  p.M = M; p.K = n; p.N = m; p.wn = n; p.wm = m; p.r = r; p.s = s;
   launch_linear_gemm(false, p, tab, stream);
 }
 
+// g is M x m_pad (m_pad = m, or m rounded up to 64 with zero columns when
+// m % 8 != 0, so every 16-byte chunk of the tensor is whole).
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
-                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m, int r,
-                       float s, const Nf4Table& tab, hipStream_t stream) {
+                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
+                       int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream) {
   GemmArgs p{};
   p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = At; p.lora_b = v; p.out = gx;
-  p.M = M; p.K = m; p.N = n; p.wn = n; p.r = r; p.s = s;
+  p.M = M; p.K = m_pad; p.N = n; p.wn = n; p.wm = m; p.r = r; p.s = s;
   launch_linear_gemm(true, p, tab, stream);
 }
 

@@ -259,6 +259,16 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restric
   }
 }
 
+// out[r][0:cols] = in[r][0:cols], out[r][cols:cols_pad] = 0 (bf16 rows)
+__global__ __launch_bounds__(256) void pad_cols_bf16_kernel(const uint16_t* __restrict__ in, int64_t rows,
+                                                            int64_t cols, int64_t cols_pad,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cols_pad) return;
+  const int64_t r = i / cols_pad, c = i % cols_pad;
+  out[i] = c < cols ? in[r * cols + c] : (uint16_t)0;
+}
+
 // out[c][r] = in[r][c] for a rows x cols bf16 matrix
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t rows,
                                                              int64_t cols, uint16_t* __restrict__ out) {
@@ -319,6 +329,13 @@ void launch_lora_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, i
   const int64_t count = J * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, nsplit, J, R,
                      s, transpose_out, out);
+}
+
+void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
+                          hipStream_t stream) {
+  const int64_t count = rows * cols_pad;
+  hipLaunchKernelGGL(pad_cols_bf16_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, in, rows, cols,
+                     cols_pad, out);
 }
 
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t stream) {

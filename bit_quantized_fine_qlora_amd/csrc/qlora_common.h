@@ -121,6 +121,25 @@ __device__ __forceinline__ void mag_dequant8(const MagLut& L, uint32_t w, uint32
   out[3] = __builtin_amdgcn_perm(H47, L47, 0x07030602u);
 }
 
+
+// Raw buffer access with a byte range: lanes whose offset is past `bytes`
+// read 0 instead of touching memory.  All offsets go in the per-lane VGPR
+// offset (the range check covers it).
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+
+__device__ __forceinline__ brsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(brsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload32(brsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(brsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);
