@@ -22,15 +22,14 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream);
-int skinny_splits(int64_t M, int64_t K);
-int64_t skinny_kc(int64_t K, int splits);
-void launch_skinny_nt(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
+int down_proj_splits(int64_t M, int64_t K, int R);
+void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
                       float* out, hipStream_t stream);
-int grad_splits(int64_t M, int64_t J);
-int64_t grad_tc(int64_t M, int splits);
-void launch_lora_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, float s, int splits,
-                      float* part, int transpose_out, uint16_t* out, hipStream_t stream);
-void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t stream);
+int token_grad_splits(int64_t M, int64_t J, int R);
+void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
+                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream);
+void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
+                           hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
                           hipStream_t stream);
 
@@ -155,7 +154,7 @@ struct FwdWs {
 FwdWs fwd_ws(int64_t M, int64_t n, int32_t r) {
   WsLayout L;
   FwdWs w;
-  w.splits = skinny_splits(M, n);
+  w.splits = down_proj_splits(M, n, r);
   w.part = L.take((size_t)w.splits * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
   w.total = L.total;
@@ -165,29 +164,29 @@ FwdWs fwd_ws(int64_t M, int64_t n, int32_t r) {
 struct BwdWs {
   size_t At, Bt, part_uv, u, v, gA, gB, gpad, total;
   int su, sv, sa, sb;
-  int64_t m_pad;  // g's row length as the input-gradient GEMM reads it
+  int64_t m_pad;  // row length of g as the kernels read it
 };
 
 BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   WsLayout L;
   BwdWs w;
-  w.su = skinny_splits(M, n);
-  w.sv = skinny_splits(M, m);
-  w.sa = grad_splits(M, n);
-  w.sb = grad_splits(M, m);
+  // The kernels read g in 16-byte pieces; rows whose length is not a
+  // multiple of 8 are first copied into a zero-padded buffer of row length m
+  // rounded up to 64 (the padded columns contribute nothing).
+  w.m_pad = (m % 8 == 0) ? m : ((m + 63) / 64) * 64;
+  w.gpad = (m % 8 == 0) ? 0 : L.take((size_t)M * w.m_pad * 2);
+  w.su = down_proj_splits(M, n, r);
+  w.sv = down_proj_splits(M, w.m_pad, r);
+  w.sa = token_grad_splits(M, n, r);
+  w.sb = token_grad_splits(M, w.m_pad, r);
   w.At = L.take((size_t)n * r * 2);
-  w.Bt = L.take((size_t)m * r * 2);
+  w.Bt = L.take((size_t)w.m_pad * r * 2);
   const int suv = w.su > w.sv ? w.su : w.sv;
   w.part_uv = L.take((size_t)suv * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
   w.v = L.take((size_t)M * r * sizeof(float));
   w.gA = L.take((size_t)w.sa * n * r * sizeof(float));
-  w.gB = L.take((size_t)w.sb * m * r * sizeof(float));
-  // The input-gradient GEMM reads g in 16-byte chunks with a per-dword range
-  // check; rows whose length is not a multiple of 8 are first copied into a
-  // zero-padded buffer of row length m rounded up to 64.
-  w.m_pad = (m % 8 == 0) ? m : ((m + 63) / 64) * 64;
-  w.gpad = (m % 8 == 0) ? 0 : L.take((size_t)M * w.m_pad * 2);
+  w.gB = L.take((size_t)w.sb * w.m_pad * r * sizeof(float));
   w.total = L.total;
   return w;
 }
@@ -277,8 +276,8 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   float* u = u_out ? u_out : at<float>(workspace, w.u);
   {
-    Timed tm("skinny_nt", hs);
-    launch_skinny_nt(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs);
+    Timed tm("down_proj", hs);
+    launch_down_proj(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs);
   }
   {
     Timed tm("fwd_gemm", hs);
@@ -304,10 +303,18 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   float* part = at<float>(workspace, w.part_uv);
+  const int64_t mk = w.m_pad;
+  const uint16_t* gk = g;
+  if (mk != m) {
+    Timed tp("transpose", hs);
+    uint16_t* gp = at<uint16_t>(workspace, w.gpad);
+    launch_pad_cols_bf16(g, M, m, mk, gp, hs);
+    gk = gp;
+  }
   const float* uu = u;
   if (!uu) {
-    Timed tm("skinny_nt", hs);
-    launch_skinny_nt(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs);
+    Timed tm("down_proj", hs);
+    launch_down_proj(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs);
     uu = at<float>(workspace, w.u);
   }
   uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
@@ -315,31 +322,24 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   float* v = at<float>(workspace, w.v);
   {
     Timed tm("transpose", hs);
-    launch_transpose_bf16(B, m, r, Bt, hs);
+    launch_transpose_bf16(B, m, r, mk, Bt, hs);
   }
   {
-    Timed tm("skinny_nt", hs);
-    launch_skinny_nt(g, M, m, Bt, r, part, w.sv, v, hs);
+    Timed tm("down_proj", hs);
+    launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs);
   }
   {
-    Timed tm("lora_grad", hs);
-    launch_lora_grad(x, M, n, v, r, s, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs);
+    Timed tm("token_grad", hs);
+    launch_token_grad(x, M, n, n, v, r, s, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs);
   }
   {
-    Timed tm("lora_grad", hs);
-    launch_lora_grad(g, M, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
+    Timed tm("token_grad", hs);
+    launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
   }
   if (grad_x) {
     {
       Timed tm("transpose", hs);
-      launch_transpose_bf16(A, r, n, At, hs);
-    }
-    const uint16_t* gk = g;
-    if (w.m_pad != m) {
-      Timed tp("transpose", hs);
-      uint16_t* gp = at<uint16_t>(workspace, w.gpad);
-      launch_pad_cols_bf16(g, M, m, w.m_pad, gp, hs);
-      gk = gp;
+      launch_transpose_bf16(A, r, n, r, At, hs);
     }
     Timed tm("dgrad_gemm", hs);
     launch_dgrad_gemm(gk, codes, absmax8, c2, At, v, grad_x, M, n, m, w.m_pad, r, s, table(), hs);

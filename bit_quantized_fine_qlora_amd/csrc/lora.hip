@@ -1,5 +1,5 @@
 // The rank-r adapter products of the adapted linear layer.
-//   u = x A^T, v = g B             (down-projections, split over K)
+//   u = x A^T, v = g B                   (down-projections, split over K)
 //   grad_A = s v^T x, grad_B = s g^T u   (reductions over tokens)
 // "QLoRA: Efficient Fine-Tuning", Step 3 (Eq. 3, the low-rank term B A x)
 // and Step 4 (Eq. 5, the adapter gradients), with the alpha/r scale of the
@@ -7,102 +7,129 @@
 // fp32 operands (u, v) enter as a bf16 hi + lo pair.  Every reduction over a
 // split dimension goes through fp32 partials summed in a fixed order, so
 // results are deterministic.
+//
+// Both kernels stream one large bf16 matrix (x or g) from HBM exactly once
+// and are bound by that read.  Each workgroup stages 16 KB tiles through LDS
+// with line-coalesced 16-byte loads (a wave covers 4 rows x 256 B), keeps
+// the next tile's loads in flight in registers while the MFMAs consume the
+// current one, and reads MFMA fragments out of XOR-swizzled LDS rows.
 #include "qlora_common.h"
 
 namespace qlora {
 
-// ---------------------------------------------------------------------------
-// out_part[split][t][q] = sum_{k in split} X[t][k] * Y[q][k]
-// X: M x K bf16 (row stride K), Y: R x K bf16.  Workgroup: 64 tokens (16 per
-// wave) x all R columns, K range [split*kc, split*kc + kc) walked in 256-wide
-// chunks with the Y chunk staged in LDS (chunk index XOR-swizzled by row).
-// ---------------------------------------------------------------------------
-namespace sk {
-constexpr int KCH = 256;                 // K per LDS chunk
-constexpr int YROWB = KCH * 2;           // 512 B
-}  // namespace sk
+__host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-__global__ __launch_bounds__(256) void skinny_nt_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+// Offset of 16-byte piece c (0..15) of row `row` in a tile of 256-byte rows;
+// any 16 consecutive rows read at one piece index hit 16 distinct bank groups.
+__device__ __forceinline__ uint32_t sw256(int row, int c) {
+  return (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4));
+}
+
+// ---------------------------------------------------------------------------
+// part[split][t][q] = sum_{k in split} X[t][k] * Y[q][k]
+// X: M x K bf16 (K a multiple of 8), Y: R x K bf16, R <= 16 * RB.
+// Workgroup: 64 tokens (16 per wave) x all R columns; its K range
+// [split * kc, split * kc + kc) is walked in stages of 128.
+// ---------------------------------------------------------------------------
+namespace dp {
+constexpr int TT = 64;        // tokens per workgroup
+constexpr int KCH = 128;      // k per stage
+constexpr int XB = TT * 256;  // X tile bytes per stage
+}  // namespace dp
+
+template <int RB>
+__global__ __launch_bounds__(256) void down_proj_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         const uint16_t* __restrict__ Y, int R,
                                                         float* __restrict__ part, int64_t kc) {
-  __shared__ __align__(16) uint8_t sY[kMaxRank * sk::YROWB];  // 64 KB
+  constexpr int YB = RB * 16 * 256;
+  constexpr int STAGE = dp::XB + YB;
+  __shared__ __align__(16) uint8_t lds[2 * STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 15;
   const int lk = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int64_t t0 = (int64_t)blockIdx.x * dp::TT;
   const int split = blockIdx.y;
   const int64_t kbeg = (int64_t)split * kc;
   const int64_t kend = (kbeg + kc < K) ? kbeg + kc : K;
-  const int RB = (R + 15) >> 4;
-  const int Rp = RB * 16;
-  const int64_t t = t0 + 16 * wave + lr;  // token row this lane feeds to MFMA
-  const bool t_ok = t < M;
-  const bool kvec = (K & 7) == 0;
+  const int nst = (int)cdiv(kend - kbeg, dp::KCH);
 
-  f32x4 acc[8];
+  const uint32_t xbytes = (uint32_t)(M * K * 2);
+  const uint32_t ybytes = (uint32_t)((int64_t)R * K * 2);
+  const brsrc_t rx = make_rsrc(X, xbytes);
+  const brsrc_t ry = make_rsrc(Y, ybytes);
+  // Load i of a stage covers row 16 i + prow, 16-byte piece pc (k offset 8 pc).
+  const int prow = tid >> 4;
+  const int pc = tid & 15;
+  const int64_t kl = kbeg + 8 * pc;
+  uint32_t xo[4], yo[RB];
+  bool rowok[4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t kb = kbeg; kb < kend; kb += sk::KCH) {
-    __syncthreads();
-    // stage Y[0:Rp][kb : kb+256] (zero past R or K)
-    for (int id = tid; id < Rp * 32; id += 256) {
-      const int row = id >> 5, c = id & 31;
-      const int64_t k = kb + 8 * c;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < R) {
-        const uint16_t* src = Y + (int64_t)row * K + k;
-        if (kvec && k + 8 <= kend) {
-          v = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int e = 0; e < 8; ++e)
-            if (k + e < kend) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-          v = u32x4{w[0], w[1], w[2], w[3]};
-        }
-      }
-      *reinterpret_cast<u32x4*>(sY + row * sk::YROWB + ((c ^ (row & 7)) << 4)) = v;
-    }
-    __syncthreads();
-#pragma unroll 2
-    for (int s8 = 0; s8 < sk::KCH / 32; ++s8) {
-      const int64_t k = kb + 32 * s8 + 8 * lk;
-      u32x4 a = u32x4{0u, 0u, 0u, 0u};
-      if (t_ok) {
-        const uint16_t* src = X + t * K + k;
-        if (kvec && k + 8 <= kend) {
-          a = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int e = 0; e < 8; ++e)
-            if (k + e < kend) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-          a = u32x4{w[0], w[1], w[2], w[3]};
-        }
-      }
-      const int c = 4 * s8 + lk;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        if (cb < RB) {
-          const int row = 16 * cb + lr;
-          const u32x4 b = *reinterpret_cast<const u32x4*>(sY + row * sk::YROWB + ((c ^ (row & 7)) << 4));
-          acc[cb] = mfma16x16x32(a, b, acc[cb]);
-        }
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    rowok[i] = t0 + 16 * i + prow < M;
+    xo[i] = (uint32_t)(((t0 + 16 * i + prow) * K + kl) * 2);
   }
-  // lane holds rows (tokens) 16*wave + 4*lk + e, column q = 16*cb + lr
+#pragma unroll
+  for (int i = 0; i < RB; ++i) yo[i] = (uint32_t)(((int64_t)(16 * i + prow) * K + kl) * 2);
+
+  auto load = [&](int st, u32x4(&xr)[4], u32x4(&yr)[RB]) {
+    const bool ok = kl + (int64_t)st * dp::KCH < kend;  // pieces past the split read as 0
+    const uint32_t d = (uint32_t)st * (dp::KCH * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = bload128(rx, (ok && rowok[i]) ? xo[i] + d : xbytes);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) yr[i] = bload128(ry, ok ? yo[i] + d : ybytes);
+  };
+  auto store = [&](int buf, const u32x4(&xr)[4], const u32x4(&yr)[RB]) {
+    uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + sw256(16 * i + prow, pc)) = xr[i];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) *reinterpret_cast<u32x4*>(base + dp::XB + sw256(16 * i + prow, pc)) = yr[i];
+  };
+
+  f32x4 acc[RB];
+#pragma unroll
+  for (int c = 0; c < RB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf) {
+    const uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(base + sw256(16 * wave + lr, 4 * s + lk));
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(base + dp::XB + sw256(16 * cb + lr, 4 * s + lk));
+        acc[cb] = mfma16x16x32(a, b, acc[cb]);
+      }
+    }
+  };
+
+  u32x4 xa[4], ya[RB], xb[4], yb[RB];
+  load(0, xa, ya);
+  if (nst > 1) load(1, xb, yb);
+  for (int st = 0; st < nst; st += 2) {
+    store(0, xa, ya);
+    if (st + 2 < nst) load(st + 2, xa, ya);
+    __syncthreads();
+    compute(0);
+    if (st + 1 >= nst) break;
+    store(1, xb, yb);
+    if (st + 3 < nst) load(st + 3, xb, yb);
+    __syncthreads();
+    compute(1);
+  }
+
+  // lane holds tokens 16*wave + 4*lk + e, column q = 16*cb + lr
   float* dst = part + (int64_t)split * M * R;
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    if (cb >= RB) break;
+  for (int cb = 0; cb < RB; ++cb) {
     const int q = 16 * cb + lr;
     if (q >= R) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t tt = t0 + 16 * wave + 4 * lk + e;
-      if (tt < M) dst[tt * R + q] = acc[cb][e];
+      const int64_t t = t0 + 16 * wave + 4 * lk + e;
+      if (t < M) dst[t * R + q] = acc[cb][e];
     }
   }
 }
@@ -119,143 +146,197 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // part[split][j][q] = sum_{t in split} X[t][j] * Y[t][q]
-// X: M x J bf16, Y: M x R fp32.  Workgroup: 256 columns j (64 per wave) x all
-// R, token range of the split walked 64 at a time.  The X tile [64 t][256 j]
-// is staged in its natural layout and read transposed (ds_read_b64_tr_b16);
-// Y is staged transposed as bf16 hi and lo planes [q][t].
+// X: M x J bf16 (J a multiple of 8), Y: M x R fp32, R <= 16 * RB.
+// Workgroup: 128 columns j (32 per wave) x all R; its token range is walked
+// in stages of 64.  The X tile keeps its natural [t][j] layout (32-byte units
+// of each row XOR-swizzled) and is read transposed with ds_read_b64_tr_b16;
+// the Y tile is split into bf16 hi and lo planes stored transposed [q][t].
 // ---------------------------------------------------------------------------
-namespace lg {
-constexpr int TT = 64;
-constexpr int XROWB = 256 * 2 + 32;   // padded row of the X tile
-constexpr int XTILEB = TT * XROWB;    // 34816
-constexpr int YROWB = TT * 2;         // 128 B per q row
-constexpr int YPLANEB = kMaxRank * YROWB;  // 16 KB
-}  // namespace lg
+namespace tg {
+constexpr int TT = 64;        // tokens per stage
+constexpr int JT = 128;       // columns per workgroup
+constexpr int XB = TT * 256;  // X tile bytes per stage
+}  // namespace tg
 
-__global__ __launch_bounds__(256) void lora_grad_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t J,
-                                                        const float* __restrict__ Y, int R,
-                                                        float* __restrict__ part, int64_t tc) {
-  __shared__ __align__(16) uint8_t sX[lg::XTILEB];
-  __shared__ __align__(16) uint8_t sYh[lg::YPLANEB];
-  __shared__ __align__(16) uint8_t sYl[lg::YPLANEB];
+// X tile: row t, 16-byte piece c (columns 8c..8c+7).  Rows t, t+1, t+2, t+3,
+// t+8, .. t+11 put a given 32-byte unit in 8 different bank groups.
+__device__ __forceinline__ uint32_t swtg(int t, int c) {
+  const int f = (t & 3) | (((t >> 3) & 1) << 2);
+  return (uint32_t)(t * 256 + ((((c >> 1) ^ f)) << 5) + ((c & 1) << 4));
+}
+// Y planes: row q holds 64 tokens (128 B) in 16-byte chunks of 8 tokens.
+__device__ __forceinline__ uint32_t swy(int q, int chunk) {
+  return (uint32_t)(q * 128 + ((chunk ^ ((q >> 1) & 7)) << 4));
+}
+
+template <int RB>
+__global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t J,
+                                                         const float* __restrict__ Y, int R,
+                                                         float* __restrict__ part, int64_t tc) {
+  constexpr int PLANE = RB * 16 * 128;
+  constexpr int STAGE = tg::XB + 2 * PLANE;
+  __shared__ __align__(16) uint8_t lds[2 * STAGE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int lr = lane & 15;
   const int lk = lane >> 4;
-  const int64_t j0 = (int64_t)blockIdx.x * 256;
+  const int64_t j0 = (int64_t)blockIdx.x * tg::JT;
   const int split = blockIdx.y;
   const int64_t tbeg = (int64_t)split * tc;
   const int64_t tend = (tbeg + tc < M) ? tbeg + tc : M;
-  const int RB = (R + 15) >> 4;
-  const int Rp = RB * 16;
-  const bool jvec = (J & 7) == 0;
-  const int tr_row = lr >> 2;
-  const int tr_col = 4 * (lr & 3);
+  const int nst = (int)cdiv(tend - tbeg, tg::TT);
 
-  f32x4 acc[4][8];
+  const uint32_t xbytes = (uint32_t)(M * J * 2);
+  const uint32_t ybytes = (uint32_t)(M * R * 4);
+  const brsrc_t rx = make_rsrc(X, xbytes);
+  const brsrc_t ry = make_rsrc(Y, ybytes);
+  const int prow = tid >> 4;
+  const int pc = tid & 15;
+  const bool jok = j0 + 8 * pc < J;
+  uint32_t xo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) xo[i] = (uint32_t)(((tbeg + 16 * i + prow) * J + j0 + 8 * pc) * 2);
+  const int ypieces = 16 * R;  // 16-byte pieces of fp32 in one 64-token Y tile
 
-  for (int64_t tb = tbeg; tb < tend; tb += lg::TT) {
-    __syncthreads();
-    // X tile: 64 rows x 32 chunks of 16 B
-    for (int id = tid; id < lg::TT * 32; id += 256) {
-      const int row = id >> 5, c = id & 31;
-      const int64_t t = tb + row;
-      const int64_t j = j0 + 8 * c;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (t < tend) {
-        const uint16_t* src = X + t * J + j;
-        if (jvec && j + 8 <= J) {
-          v = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-          for (int e = 0; e < 8; ++e)
-            if (j + e < J) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-          v = u32x4{w[0], w[1], w[2], w[3]};
+  // Planes rows q in [R, 16 RB) are never written by the stages: clear them.
+  for (int id = tid; id < 2 * 2 * (16 * RB - R) * 8; id += 256) {
+    const int chunk = id & 7;
+    const int rest = id >> 3;
+    const int q = R + rest % (16 * RB - R);
+    const int pl = rest / (16 * RB - R);  // stage * 2 + plane
+    *reinterpret_cast<u32x4*>(lds + (pl >> 1) * STAGE + tg::XB + (pl & 1) * PLANE + swy(q, chunk)) =
+        u32x4{0u, 0u, 0u, 0u};
+  }
+
+  auto load = [&](int st, u32x4(&xr)[4], u32x4(&yr)[RB]) {
+    const int64_t tb = tbeg + (int64_t)st * tg::TT;
+    const uint32_t d = (uint32_t)(st * tg::TT * J * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = jok && (tb + 16 * i + prow < tend);
+      xr[i] = bload128(rx, ok ? xo[i] + d : xbytes);
+    }
+    const uint32_t ybase = (uint32_t)(tb * R * 4);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int p = 256 * i + tid;
+      yr[i] = bload128(ry, p < ypieces ? ybase + 16 * p : ybytes);
+    }
+  };
+  auto store = [&](int buf, int st, const u32x4(&xr)[4], const u32x4(&yr)[RB]) {
+    uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + swtg(16 * i + prow, pc)) = xr[i];
+    const int64_t tb = tbeg + (int64_t)st * tg::TT;
+    const int tlim = (int)((tend - tb) < tg::TT ? (tend - tb) : tg::TT);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int p = 256 * i + tid;
+      if (p < ypieces) {
+        int f = 4 * p;
+        int t = f / R;
+        int q = f - t * R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y = t < tlim ? __uint_as_float(yr[i][e]) : 0.0f;
+          float h, l;
+          split_bf16(y, h, l);
+          const uint32_t off = swy(q, t >> 3) + (t & 7) * 2;
+          *reinterpret_cast<uint16_t*>(base + tg::XB + off) = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+          *reinterpret_cast<uint16_t*>(base + tg::XB + PLANE + off) = (uint16_t)(pack_bf16x2(l, 0.f) & 0xFFFFu);
+          if (++q == R) { q = 0; ++t; }
         }
       }
-      *reinterpret_cast<u32x4*>(sX + row * lg::XROWB + 16 * c) = v;
     }
-    // Y tile transposed into bf16 hi / lo planes; chunk of 8 tokens XOR-swizzled by q
-    for (int id = tid; id < lg::TT * Rp; id += 256) {
-      const int trow = id / Rp, q = id % Rp;
-      const int64_t t = tb + trow;
-      const float y = (t < tend && q < R) ? Y[t * R + q] : 0.0f;
-      float h, l;
-      split_bf16(y, h, l);
-      const uint32_t off = q * lg::YROWB + ((((trow >> 3) ^ (q & 7))) << 4) + (trow & 7) * 2;
-      *reinterpret_cast<uint16_t*>(sYh + off) = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
-      *reinterpret_cast<uint16_t*>(sYl + off) = (uint16_t)(pack_bf16x2(l, 0.f) & 0xFFFFu);
-    }
-    __syncthreads();
+  };
+
+  f32x4 acc[2][RB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < RB; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tr_row = lr >> 2;
+  const int tr_c = lr & 3;
+  auto compute = [&](int buf) {
+    const uint8_t* base = lds + buf * STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4 a[4];
+      u32x4 a[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int trow = 32 * kk + 8 * lk + tr_row;
-        const int jcol = 64 * wave + 16 * i + tr_col;
-        uint8_t* base = sX + trow * lg::XROWB + jcol * 2;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * lg::XROWB));
+      for (int ib = 0; ib < 2; ++ib) {
+        // lanes 4r+c of each 16-lane group address row r, columns 4c..4c+3
+        const int t = 32 * kk + 8 * lk + tr_row;
+        const int c = 2 * (2 * wave + ib) + (tr_c >> 1);
+        const uint8_t* p0 = base + swtg(t, c) + (tr_c & 1) * 8;
+        const uint8_t* p1 = base + swtg(t + 4, c) + (tr_c & 1) * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        a[i] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        a[ib] = u32x4{l2[0], l2[1], h2[0], h2[1]};
       }
-      const int c = 4 * kk + lk;
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        if (cb < RB) {
-          const int q = 16 * cb + lr;
-          const uint32_t off = q * lg::YROWB + ((c ^ (q & 7)) << 4);
-          const u32x4 bh = *reinterpret_cast<const u32x4*>(sYh + off);
-          const u32x4 bl = *reinterpret_cast<const u32x4*>(sYl + off);
+      for (int cb = 0; cb < RB; ++cb) {
+        const uint32_t off = swy(16 * cb + lr, 4 * kk + lk);
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(base + tg::XB + off);
+        const u32x4 bl = *reinterpret_cast<const u32x4*>(base + tg::XB + PLANE + off);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i][cb] = mfma16x16x32(a[i], bh, acc[i][cb]);
-            acc[i][cb] = mfma16x16x32(a[i], bl, acc[i][cb]);
-          }
+        for (int ib = 0; ib < 2; ++ib) {
+          acc[ib][cb] = mfma16x16x32(a[ib], bh, acc[ib][cb]);
+          acc[ib][cb] = mfma16x16x32(a[ib], bl, acc[ib][cb]);
         }
       }
     }
+  };
+
+  u32x4 xa[4], ya[RB], xb[4], yb[RB];
+  load(0, xa, ya);
+  if (nst > 1) load(1, xb, yb);
+  for (int st = 0; st < nst; st += 2) {
+    store(0, st, xa, ya);
+    if (st + 2 < nst) load(st + 2, xa, ya);
+    __syncthreads();
+    compute(0);
+    if (st + 1 >= nst) break;
+    store(1, st + 1, xb, yb);
+    if (st + 3 < nst) load(st + 3, xb, yb);
+    __syncthreads();
+    compute(1);
   }
-  // lane holds rows j = 64*wave + 16*i + 4*lk + e, column q = 16*cb + lr
+
+  // lane holds columns j = 32*wave + 16*ib + 4*lk + e, q = 16*cb + lr
   float* dst = part + (int64_t)split * J * R;
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    if (cb >= RB) break;
+  for (int cb = 0; cb < RB; ++cb) {
     const int q = 16 * cb + lr;
     if (q >= R) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t j = j0 + 64 * wave + 16 * i + 4 * lk + e;
-        if (j < J) dst[j * R + q] = acc[i][cb][e];
+        const int64_t j = j0 + 32 * wave + 16 * ib + 4 * lk + e;
+        if (j < J) dst[j * R + q] = acc[ib][cb][e];
       }
   }
 }
 
-// out = bf16(s * sum_s part[s]); part is [J][R]; out is [J][R] or, when
-// transpose_out, [R][J].
+// out = bf16(s * sum_s part[s]) over the first Jout rows of part ([J][R] per
+// split); out is [Jout][R] or, when transpose_out, [R][Jout].
 __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restrict__ part, int nsplit, int64_t J,
-                                                          int R, float s, int transpose_out,
+                                                          int64_t Jout, int R, float s, int transpose_out,
                                                           uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t count = J * R;
-  if (i >= count) return;
+  if (i >= Jout * R) return;
+  const int64_t stride = J * R;
   float acc = 0.0f;
-  for (int k = 0; k < nsplit; ++k) acc += part[(int64_t)k * count + i];
+  for (int k = 0; k < nsplit; ++k) acc += part[(int64_t)k * stride + i];
   const uint16_t b = (uint16_t)(pack_bf16x2(s * acc, 0.f) & 0xFFFFu);
   if (!transpose_out) {
     out[i] = b;
   } else {
     const int64_t j = i / R, q = i % R;
-    out[q * J + j] = b;
+    out[q * Jout + j] = b;
   }
 }
 
@@ -269,66 +350,72 @@ __global__ __launch_bounds__(256) void pad_cols_bf16_kernel(const uint16_t* __re
   out[i] = c < cols ? in[r * cols + c] : (uint16_t)0;
 }
 
-// out[c][r] = in[r][c] for a rows x cols bf16 matrix
+// out[c][r] = in[r][c] for a rows x cols bf16 matrix; out rows have length
+// ld >= rows and out[c][rows:ld] = 0.  One thread per output element.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t rows,
-                                                             int64_t cols, uint16_t* __restrict__ out) {
+                                                             int64_t cols, int64_t ld, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * cols) return;
-  const int64_t r = i / cols, c = i % cols;
-  out[c * rows + r] = in[i];
+  if (i >= cols * ld) return;
+  const int64_t c = i / ld, r = i % ld;
+  out[i] = r < rows ? in[r * cols + c] : (uint16_t)0;
 }
 
 // ---------------------------------------------------------------------------
 // host-side launch helpers
 // ---------------------------------------------------------------------------
-static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int rank_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8; }
+// Workgroups wanted per launch: enough to cover every CU a few times over
+// (fewer for the large-rank variants, which hold one workgroup per CU).
+static inline int64_t target_wgs(int R) { return rank_blocks(R) <= 2 ? 512 : 256; }
 
-int skinny_splits(int64_t M, int64_t K) {
-  const int64_t tiles = cdiv(M, 64);
-  const int64_t chunks = cdiv(K, sk::KCH);
-  int64_t want = cdiv(1024, tiles);
+int down_proj_splits(int64_t M, int64_t K, int R) {
+  const int64_t tiles = cdiv(M, dp::TT);
+  const int64_t stages = cdiv(K, dp::KCH);
+  int64_t want = cdiv(target_wgs(R), tiles);
   if (want < 1) want = 1;
-  if (want > chunks) want = chunks;
+  if (want > stages) want = stages;
   if (want > 64) want = 64;
-  return (int)want;
+  return (int)cdiv(K, cdiv(cdiv(K, want), dp::KCH) * dp::KCH);
 }
 
-int64_t skinny_kc(int64_t K, int splits) {
-  return cdiv(cdiv(K, splits), sk::KCH) * sk::KCH;
-}
-
-void launch_skinny_nt(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
+void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
                       float* out, hipStream_t stream) {
-  const int64_t kc = skinny_kc(K, splits);
-  const int nsplit = (int)cdiv(K, kc);
-  hipLaunchKernelGGL(skinny_nt_kernel, dim3((unsigned)cdiv(M, 64), (unsigned)nsplit), dim3(256), 0, stream, X, M, K,
-                     Y, R, part, kc);
+  const int64_t kc = cdiv(cdiv(K, splits), dp::KCH) * dp::KCH;
+  const dim3 grid((unsigned)cdiv(M, dp::TT), (unsigned)splits);
+  switch (rank_blocks(R)) {
+    case 1: hipLaunchKernelGGL(down_proj_kernel<1>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+    case 2: hipLaunchKernelGGL(down_proj_kernel<2>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+    case 4: hipLaunchKernelGGL(down_proj_kernel<4>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+    default: hipLaunchKernelGGL(down_proj_kernel<8>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+  }
   const int64_t count = M * R;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, nsplit,
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
                      count, out);
 }
 
-int grad_splits(int64_t M, int64_t J) {
-  const int64_t tiles = cdiv(J, 256);
-  const int64_t chunks = cdiv(M, lg::TT);
-  int64_t want = cdiv(768, tiles);
+int token_grad_splits(int64_t M, int64_t J, int R) {
+  const int64_t tiles = cdiv(J, tg::JT);
+  const int64_t stages = cdiv(M, tg::TT);
+  int64_t want = cdiv(target_wgs(R), tiles);
   if (want < 1) want = 1;
-  if (want > chunks) want = chunks;
+  if (want > stages) want = stages;
   if (want > 64) want = 64;
-  return (int)want;
+  return (int)cdiv(M, cdiv(cdiv(M, want), tg::TT) * tg::TT);
 }
 
-int64_t grad_tc(int64_t M, int splits) { return cdiv(cdiv(M, splits), lg::TT) * lg::TT; }
-
-void launch_lora_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, float s, int splits,
-                      float* part, int transpose_out, uint16_t* out, hipStream_t stream) {
-  const int64_t tc = grad_tc(M, splits);
-  const int nsplit = (int)cdiv(M, tc);
-  hipLaunchKernelGGL(lora_grad_kernel, dim3((unsigned)cdiv(J, 256), (unsigned)nsplit), dim3(256), 0, stream, X, M, J,
-                     Y, R, part, tc);
-  const int64_t count = J * R;
-  hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, nsplit, J, R,
-                     s, transpose_out, out);
+void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
+                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream) {
+  const int64_t tc = cdiv(cdiv(M, splits), tg::TT) * tg::TT;
+  const dim3 grid((unsigned)cdiv(J, tg::JT), (unsigned)splits);
+  switch (rank_blocks(R)) {
+    case 1: hipLaunchKernelGGL(token_grad_kernel<1>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
+    case 2: hipLaunchKernelGGL(token_grad_kernel<2>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
+    case 4: hipLaunchKernelGGL(token_grad_kernel<4>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
+    default: hipLaunchKernelGGL(token_grad_kernel<8>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
+  }
+  const int64_t count = Jout * R;
+  hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
+                     Jout, R, s, transpose_out, out);
 }
 
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
@@ -338,10 +425,11 @@ void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_
                      cols_pad, out);
 }
 
-void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t stream) {
-  const int64_t count = rows * cols;
+void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
+                           hipStream_t stream) {
+  const int64_t count = cols * ld;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, in, rows, cols,
-                     out);
+                     ld, out);
 }
 
 }  // namespace qlora

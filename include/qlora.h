@@ -153,7 +153,7 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
  * qlora_profile_enable(1) clears earlier records; (0) stops recording.
  * qlora_profile_query waits for the recorded events of kernel `name`
  * ("quantize", "dequant", "fwd_gemm", "fwd_small", "dgrad_gemm",
- * "skinny_nt", "lora_grad", "reduce", "transpose") and reports the launch
+ * "down_proj", "token_grad", "transpose") and reports the launch
  * count and the summed duration in milliseconds (host pointers).
  */
 qlora_status qlora_profile_enable(int on);
