@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     dequant_nf4_dq,
     linear_bwd,
     linear_fwd,
+    linear_fwd_grouped,
     nf4_table,
     profile_enable,
     profile_query,

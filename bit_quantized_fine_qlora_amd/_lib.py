@@ -19,6 +19,14 @@ c_f32 = ctypes.c_float
 c_vp = ctypes.c_void_p
 c_sz = ctypes.c_size_t
 
+
+class LinearLayer(ctypes.Structure):
+    """qlora_linear_layer: one layer of a grouped forward (host struct)."""
+    _fields_ = [("n", c_i64), ("m", c_i64), ("r", c_i32), ("s", c_f32),
+                ("x", c_vp), ("codes", c_vp), ("absmax8", c_vp), ("c2", c_vp),
+                ("A", c_vp), ("B", c_vp), ("h", c_vp), ("u_out", c_vp)]
+
+
 # name -> (restype, argtypes); mirrors include/qlora.h
 PROTOTYPES = {
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -29,6 +37,8 @@ PROTOTYPES = {
     "qlora_workspace_bytes": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32]),
     "qlora_linear_fwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qlora_grouped_workspace_bytes": (c_sz, [c_i64, c_i32, ctypes.POINTER(LinearLayer)]),
+    "qlora_linear_fwd_grouped": (ctypes.c_int, [c_i64, c_i32, ctypes.POINTER(LinearLayer), c_vp, c_sz, c_vp]),
     "qlora_linear_bwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),

@@ -22,6 +22,16 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream);
+int small_max_tokens();
+int small_max_layers();
+size_t small_ws_bytes(int64_t M, int64_t n, int64_t m, int r);
+struct SmallLayerHost {
+  const uint16_t* x; const uint8_t* codes; const uint8_t* absmax8; const float* c2;
+  const uint16_t* A; const uint16_t* B; uint16_t* h; float* u_out;
+  int64_t n, m; int r; float s;
+  void* ws;
+};
+void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4Table& tab, hipStream_t stream);
 int down_proj_splits(int64_t M, int64_t K, int R);
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
                       float* out, hipStream_t stream);
@@ -151,9 +161,16 @@ struct FwdWs {
   int splits;
 };
 
-FwdWs fwd_ws(int64_t M, int64_t n, int32_t r) {
+FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   WsLayout L;
   FwdWs w;
+  if (M <= small_max_tokens()) {  // weight-streaming path: fp32 partials only
+    w.splits = 0;
+    w.part = w.u = 0;
+    L.take(small_ws_bytes(M, n, m, r));
+    w.total = L.total;
+    return w;
+  }
   w.splits = down_proj_splits(M, n, r);
   w.part = L.take((size_t)w.splits * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
@@ -255,7 +272,7 @@ qlora_status qlora_dequant_nf4_dq(const uint8_t* codes, const uint8_t* absmax8, 
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r) {
   if (check_linear(M, n, m, r, 1.0f) != QLORA_OK) return 0;
-  if (op == QLORA_OP_FWD) return fwd_ws(M, n, r).total;
+  if (op == QLORA_OP_FWD) return fwd_ws(M, n, m, r).total;
   if (op == QLORA_OP_BWD) return bwd_ws(M, n, m, r).total;
   return 0;
 }
@@ -270,10 +287,16 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(A) ||
       !aligned16(B) || !aligned16(h) || (u_out && !aligned16(u_out)))
     return QLORA_ERR_ALIGN;
-  const FwdWs w = fwd_ws(M, n, r);
+  const FwdWs w = fwd_ws(M, n, m, r);
   if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (M <= small_max_tokens()) {
+    const SmallLayerHost L{x, codes, absmax8, c2, A, B, h, u_out, n, m, r, s, workspace};
+    Timed tm("fwd_small", hs);
+    launch_small_fwd((int)M, &L, 1, table(), hs);
+    return hip_status();
+  }
   float* u = u_out ? u_out : at<float>(workspace, w.u);
   {
     Timed tm("down_proj", hs);
@@ -282,6 +305,65 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   {
     Timed tm("fwd_gemm", hs);
     launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s, table(), hs);
+  }
+  return hip_status();
+}
+
+static qlora_status check_layer(int64_t M, const qlora_linear_layer& L) {
+  qlora_status st = check_linear(M, L.n, L.m, L.r, L.s);
+  if (st != QLORA_OK) return st;
+  if (!L.x || !L.codes || !L.absmax8 || !L.c2 || !L.A || !L.B || !L.h) return QLORA_ERR_NULL;
+  if (!aligned16(L.x) || !aligned16(L.codes) || !aligned16(L.absmax8) || !aligned16(L.c2) || !aligned16(L.A) ||
+      !aligned16(L.B) || !aligned16(L.h) || (L.u_out && !aligned16(L.u_out)))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+size_t qlora_grouped_workspace_bytes(int64_t M, int32_t count, const qlora_linear_layer* layers) {
+  if (!layers || count < 1 || count > small_max_layers()) return 0;
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    if (check_linear(M, layers[i].n, layers[i].m, layers[i].r, 1.0f) != QLORA_OK) return 0;
+    total += align256(fwd_ws(M, layers[i].n, layers[i].m, layers[i].r).total);
+  }
+  return total;
+}
+
+qlora_status qlora_linear_fwd_grouped(int64_t M, int32_t count, const qlora_linear_layer* layers, void* workspace,
+                                      size_t workspace_bytes, qlora_stream_t stream) {
+  if (!layers) return QLORA_ERR_NULL;
+  if (count < 1 || count > small_max_layers()) return QLORA_ERR_VALUE;
+  for (int i = 0; i < count; ++i) {
+    const qlora_status st = check_layer(M, layers[i]);
+    if (st != QLORA_OK) return st;
+  }
+  const size_t need = qlora_grouped_workspace_bytes(M, count, layers);
+  if (!workspace || workspace_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (M > small_max_tokens()) {
+    size_t off = 0;
+    for (int i = 0; i < count; ++i) {
+      const qlora_linear_layer& L = layers[i];
+      const size_t wb = align256(fwd_ws(M, L.n, L.m, L.r).total);
+      const qlora_status st = qlora_linear_fwd(M, L.n, L.m, L.r, L.s, L.x, L.codes, L.absmax8, L.c2, L.A, L.B, L.h,
+                                               L.u_out, at<uint8_t>(workspace, off), wb, stream);
+      if (st != QLORA_OK) return st;
+      off += wb;
+    }
+    return QLORA_OK;
+  }
+  SmallLayerHost H[8];
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    const qlora_linear_layer& L = layers[i];
+    H[i] = SmallLayerHost{L.x, L.codes, L.absmax8, L.c2, L.A, L.B, L.h, L.u_out, L.n, L.m, L.r, L.s,
+                          at<uint8_t>(workspace, off)};
+    off += align256(fwd_ws(M, L.n, L.m, L.r).total);
+  }
+  {
+    Timed tm("fwd_small", hs);
+    launch_small_fwd((int)M, H, count, table(), hs);
   }
   return hip_status();
 }

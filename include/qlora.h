@@ -76,7 +76,12 @@ void qlora_nf4_table(float* levels, float* thresholds);
  *   W        device, m*n fp32, row-major; blocks are 64 consecutive elements
  *            along n, groups are 256 consecutive blocks (16384 elements; the
  *            last group may be partial).
- *   codes    device out, m*n/2 bytes; element 2k in the low nibble of byte k.
+ *   codes    device out, m*n/2 bytes of 4-bit codes.  Code of level L
+ *            (0..15, ascending): bit 3 = sign (set for the 8 negative
+ *            levels), bits 0-2 = rank of |level| (L - 8 for L >= 8, 15 - L
+ *            for L < 8).  Per 8 consecutive elements e..e+7 (a 32-bit word),
+ *            byte j holds element e+j in its low nibble and e+j+4 in its high
+ *            nibble.
  *   absmax8  device out, m*n/64 bytes: E4M3FN (bias 7, RNE) of c1_b / c2_g,
  *            where c1_b is the fp32 absmax of block b.
  *   c2       device out, ceil(m*n/16384) fp32: c2_g = max c1_b over group g.
@@ -121,11 +126,52 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r)
  *   h        device out, M x m bf16.
  *   u_out    device out, M x r fp32, or NULL.  Keep it for the backward.
  *   workspace, workspace_bytes: at least qlora_workspace_bytes(0, ...).
+ * Size limits (32-bit offsets): M * max(n, m) < 2^30 and m * n < 2^31.
+ * M <= 32 takes the weight-streaming path (bound by reading the packed
+ * weight); larger M the tiled MFMA path.  Both give the same results up to
+ * fp32 summation order.
  */
 qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
                               const uint8_t* codes, const uint8_t* absmax8, const float* c2, const qlora_bf16* A,
                               const qlora_bf16* B, qlora_bf16* h, float* u_out, void* workspace,
                               size_t workspace_bytes, qlora_stream_t stream);
+
+/*
+ * One layer of a grouped forward: the arguments of qlora_linear_fwd for one
+ * weight (all device pointers, same rules).  Host struct.
+ */
+typedef struct {
+  int64_t n, m;
+  int32_t r;
+  float s;
+  const qlora_bf16* x;
+  const uint8_t* codes;
+  const uint8_t* absmax8;
+  const float* c2;
+  const qlora_bf16* A;
+  const qlora_bf16* B;
+  qlora_bf16* h;
+  float* u_out; /* may be NULL */
+} qlora_linear_layer;
+
+/*
+ * Workspace bytes for qlora_linear_fwd_grouped with these layers (host
+ * array of `count`); 0 on invalid arguments.
+ */
+size_t qlora_grouped_workspace_bytes(int64_t M, int32_t count, const qlora_linear_layer* layers);
+
+/*
+ * Forward of `count` independent adapted linear layers that share the token
+ * count M (for example the seven projections of a transformer block), each
+ * exactly as qlora_linear_fwd would compute it.  For M <= 32 the layers are
+ * streamed by one launch (plus one launch that finishes them), which keeps
+ * the GPU busy on layers too small to fill it alone; larger M runs the
+ * layers one after another.  `layers` is a host array, read before the call
+ * returns; count 1..8.  Errors as for qlora_linear_fwd, checked for every
+ * layer before anything is launched.
+ */
+qlora_status qlora_linear_fwd_grouped(int64_t M, int32_t count, const qlora_linear_layer* layers, void* workspace,
+                                      size_t workspace_bytes, qlora_stream_t stream);
 
 /*
  * Backward of the forward above for upstream gradient g = dL/dh

@@ -123,3 +123,34 @@ def test_workspace_sizes(lib):
     assert lib.qlora_workspace_bytes(0, 32, 100, 256, 8) == 0
     assert lib.qlora_workspace_bytes(7, 32, 256, 256, 8) == 0
     assert lib.qlora_workspace_bytes(0, 32, 256, 256, 0) == 0
+
+
+def layer_desc(n=256, m=256, r=8, s=2.0, x=1 << 20, h=1 << 20, u=0):
+    from bit_quantized_fine_qlora_amd import _lib
+    return _lib.LinearLayer(n, m, r, s, x, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, h, u)
+
+
+def test_grouped_argument_errors(lib):
+    from bit_quantized_fine_qlora_amd import _lib
+    f = lib.qlora_linear_fwd_grouped
+    arr = (_lib.LinearLayer * 3)(layer_desc(), layer_desc(n=512, m=128, r=16), layer_desc(m=1024))
+    need = lib.qlora_grouped_workspace_bytes(16, 3, arr)
+    assert need > 0
+    assert f(16, 3, None, P, 1 << 30, None) == -1
+    assert f(16, 0, arr, P, 1 << 30, None) == -7
+    assert f(16, 9, arr, P, 1 << 30, None) == -7
+    assert f(16, 3, arr, None, 1 << 30, None) == -5
+    assert f(16, 3, arr, P, need - 1, None) == -5
+    assert f(16, 3, arr, MIS, need, None) == -4
+    bad = (_lib.LinearLayer * 2)(layer_desc(), layer_desc(n=100))
+    assert f(16, 2, bad, P, 1 << 30, None) == -2
+    assert lib.qlora_grouped_workspace_bytes(16, 2, bad) == 0
+    bad = (_lib.LinearLayer * 2)(layer_desc(), layer_desc(r=0))
+    assert f(16, 2, bad, P, 1 << 30, None) == -3
+    bad = (_lib.LinearLayer * 2)(layer_desc(), layer_desc(x=0))
+    assert f(16, 2, bad, P, 1 << 30, None) == -1
+    bad = (_lib.LinearLayer * 2)(layer_desc(), layer_desc(u=(1 << 20) + 4))
+    assert f(16, 2, bad, P, 1 << 30, None) == -4
+    # the grouped workspace is the sum of the single-layer ones, each rounded to 256 bytes
+    singles = [lib.qlora_workspace_bytes(0, 16, d.n, d.m, d.r) for d in arr]
+    assert need == sum((b + 255) // 256 * 256 for b in singles)

@@ -109,6 +109,79 @@ def test_ragged_shapes(Q, M, n, m, r, s):
     check_full(Q, inp["W"], inp, s, label=f"ragged M={M} n={n} m={m} r={r}")
 
 
+SMALL_M = [
+    # (M, n, m, r, s) on the weight-streaming path (M <= 32): K chunks of 2048,
+    # 256-k pieces per wave, groups of 128 features
+    (16, 4096, 1024, 16, 2.0),
+    (1, 64, 33, 1, 1.0),
+    (32, 4160, 130, 17, 0.5),
+    (15, 2112, 257, 64, 0.25),
+    (31, 320, 16, 128, 0.125),
+    (16, 6144, 384, 7, 3.0),
+    (2, 128, 2000, 32, 2.0),
+]
+
+
+@pytest.mark.parametrize("M,n,m,r,s", SMALL_M)
+def test_small_token_path(Q, M, n, m, r, s):
+    inp = QI.custom_inputs(seed=M * 11 + n + m, M=M, n=n, m=m, r=r)
+    check_full(Q, inp["W"], inp, s, label=f"small-M M={M} n={n} m={m} r={r}")
+
+
+def grouped_case(Q, M, shapes, seed):
+    layers, singles = [], []
+    for i, (n, m, r, s) in enumerate(shapes):
+        inp = QI.custom_inputs(seed=seed + i, M=M, n=n, m=m, r=r)
+        q = Q.quantize_nf4_dq(torch.from_numpy(inp["W"]).to("cuda"))
+        x, A, B = dev_bf16(inp["x"]), dev_bf16(inp["A"]), dev_bf16(inp["B"])
+        layers.append((x, q, A, B, s))
+        singles.append((inp, s))
+    say(f"grouped forward M={M} layers={len(shapes)}")
+    outs = Q.linear_fwd_grouped(layers)
+    torch.cuda.synchronize()
+    for (x, q, A, B, s), (h, u), (inp, _) in zip(layers, outs, singles):
+        h1, u1 = Q.linear_fwd(x, q, A, B, s)
+        torch.cuda.synchronize()
+        assert torch.equal(h, h1) and torch.equal(u, u1), "grouped and single-layer results differ"
+        W = inp["W"]
+        ref = oracle_full(W, inp["x"], None, inp["A"], inp["B"], s)
+        assert_close(f64(host_bits(h)), ref["h"], f"grouped h {W.shape}")
+        assert_close(u.cpu().numpy(), ref["u"], f"grouped u {W.shape}")
+
+
+def test_grouped_forward_small_tokens(Q):
+    grouped_case(Q, 16, [(4096, 512, 16, 2.0), (1024, 64, 8, 1.0), (2112, 300, 16, 2.0), (256, 1024, 32, 0.5),
+                         (64, 16, 1, 4.0), (6144, 128, 64, 0.25), (512, 2048, 16, 2.0)], seed=700)
+
+
+def test_grouped_forward_large_tokens(Q):
+    grouped_case(Q, 72, [(256, 320, 16, 2.0), (512, 64, 8, 1.0)], seed=800)
+
+
+def test_grouped_full_block_matches_single_layers(Q):
+    # the seven layers of the 8B-shaped block at 16 tokens, in one grouped call
+    cfg = QI.CONFIGS[4]
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    layers = []
+    for L in cfg["layers"]:
+        W = torch.randn((L.m, L.n), generator=gen, device="cuda", dtype=torch.float32) * L.w_sigma
+        q = Q.quantize_nf4_dq(W)
+        del W
+        x = torch.randn((L.M, L.n), generator=gen, device="cuda").to(torch.bfloat16)
+        A = (torch.randn((L.r, L.n), generator=gen, device="cuda") / 16).to(torch.bfloat16)
+        B = (torch.randn((L.m, L.r), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+        layers.append((x, q, A, B, L.s))
+    say("grouped 8B block forward")
+    outs = Q.linear_fwd_grouped(layers)
+    torch.cuda.synchronize()
+    for (x, q, A, B, s), (h, u) in zip(layers, outs):
+        h1, u1 = Q.linear_fwd(x, q, A, B, s)
+        torch.cuda.synchronize()
+        assert torch.equal(h, h1) and torch.equal(u, u1)
+    del layers, outs
+    torch.cuda.empty_cache()
+
+
 def test_adapter_b_zero(Q):
     # B = 0 (the adapter's initial state): h is the plain dequant GEMM, grad_A is exactly 0
     inp = QI.custom_inputs(seed=3, M=96, n=256, m=320, r=16)
