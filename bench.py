@@ -8,6 +8,14 @@ grad_B).  Workload: the Llama-3.1-8B-shaped gate projection, W0 14336 x
 
 value = algorithmic forward + backward flops per step / step time (TFLOP/s),
 the quantizer's time included in the step.  Prints one JSON line.
+
+Besides the timed steps (and outside them) it also measures, each with HIP
+events on the stream the library launches on:
+  - the forward alone and the backward alone of the same layer;
+  - the small-token regime: the forward of all seven layers of the
+    8B-shaped block at 16 tokens in one grouped call, and the quantization of
+    the block's seven weights, both against the HBM peak (the caches are
+    flushed by writing 1 GiB before every repetition).
 """
 
 from __future__ import annotations
@@ -25,6 +33,31 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per launch of the GEMM kernels on this workload, from rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch),
+# scaled by what the same counters read for a plain 1 GiB device copy
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/).  Valid only for the
+# GEMM source they were taken on: reported as null once it changes.
+GEMM_SRC = os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", "gemm_linear.hip")
+GEMM_TRAFFIC = {
+    "src_sha1": "3207302a681d3a39b98a675dfe6888406df027bf",
+    "fwd_gemm": {"fetch": 2 * 297272.06 * 1024, "write": 117635.64 * 1024},
+    "dgrad_gemm": {"fetch": 2 * 176958.81 * 1024, "write": 33824.61 * 1024},
+}
+
+
+def gemm_traffic(kernel):
+    import hashlib
+    try:
+        with open(GEMM_SRC, "rb") as f:
+            digest = hashlib.sha1(f.read()).hexdigest()
+    except OSError:
+        return None
+    if digest != GEMM_TRAFFIC["src_sha1"] or kernel not in GEMM_TRAFFIC:
+        return None
+    t = GEMM_TRAFFIC[kernel]
+    return int(t["fetch"] + t["write"])
+
 
 def fwd_flops(M, n, m, r):
     return 2 * M * m * n + 2 * M * r * (m + n)
@@ -37,6 +70,76 @@ def bwd_flops(M, n, m, r):
 def quant_bytes(m, n):
     numel = m * n
     return 4 * numel + numel // 2 + numel // 64 + 4 * ((numel // 64 + 255) // 256)
+
+
+def small_forward_bytes(layers, M):
+    """Algorithmic bytes of a small-token forward: packed weight + x + A + B + h."""
+    tot = 0
+    for L in layers:
+        numel = L.m * L.n
+        tot += numel // 2 + numel // 64 + 4 * ((numel // 64 + 255) // 256)
+        tot += 2 * (M * L.n + L.r * L.n + L.m * L.r + M * L.m)
+    return tot
+
+
+def timed_us(fn, reps, flush=None):
+    """Median and min of `reps` event-timed calls of fn (after one untimed call)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def small_token_block(Q, dev, reps):
+    """Forward of the 8B-shaped block (7 layers, 16 tokens) and quantization of its weights."""
+    import torch
+
+    import qlora_inputs as QI
+    cfg = QI.CONFIGS[4]
+    gen = torch.Generator(device=dev).manual_seed(4)
+    Ws, layers = [], []
+    for L in cfg["layers"]:
+        W = torch.randn((L.m, L.n), generator=gen, device=dev, dtype=torch.float32) * L.w_sigma
+        q = Q.quantize_nf4_dq(W)
+        x = torch.randn((L.M, L.n), generator=gen, device=dev).to(torch.bfloat16)
+        A = (torch.randn((L.r, L.n), generator=gen, device=dev) / 16).to(torch.bfloat16)
+        B = (torch.randn((L.m, L.r), generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+        Ws.append((W, q))
+        layers.append((x, q, A, B, L.s))
+    M = cfg["layers"][0].M
+    grouped = Q.GroupedForward(layers)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    fb = small_forward_bytes(cfg["layers"], M)
+    med, mn = timed_us(grouped.run, reps, flush)
+    qbytes = sum(quant_bytes(L.m, L.n) for L in cfg["layers"])
+
+    def quant_all():
+        for W, q in Ws:
+            Q.quantize_nf4_dq(W, out=q)
+
+    qmed, qmn = timed_us(quant_all, max(3, reps // 2), flush)
+    return {
+        "forward": {"workload": "8B-shaped block: q,k,v,o,gate,up,down, 16 tokens, r=16, one grouped call",
+                    "us": round(med, 2), "us_min": round(mn, 2), "bytes": fb,
+                    "GB/s": round(fb / (med * 1e-6) / 1e9, 1), "hbm_frac": round(fb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "quantize": {"workload": "the block's seven fp32 weights (218,103,808 params)",
+                     "us": round(qmed, 2), "bytes": qbytes,
+                     "GB/s": round(qbytes / (qmed * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(qbytes / (qmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cache_flush": "1 GiB written before every repetition",
+    }
 
 
 def cpu_baseline(cfg, layer, tokens):
@@ -79,8 +182,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the measurements outside the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -164,12 +268,21 @@ def main():
     dom_us = kern[dom]["avg_us"]
     achieved = per_launch[dom] / (dom_us * 1e-6) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic(dom)}
     qb = quant_bytes(m, n)
     quant = {"avg_us": round(kern["quantize"]["avg_us"], 2),
              "GB/s": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9, 1),
              "hbm_frac": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     other = {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()}
+
+    extra = {}
+    if not args.no_extra:
+        fwd_med, _ = timed_us(lambda: Q.linear_fwd(x, q, A, B, s, h=h, u=u, workspace=ws_f), 10)
+        bwd_med, _ = timed_us(lambda: Q.linear_bwd(x, g, q, A, B, s, u=u, out=(gx, gA, gB), workspace=ws_b), 10)
+        extra["passes"] = {
+            "forward": {"us": round(fwd_med, 2), "TFLOP/s": round(fwd_flops(M, n, m, r) / (fwd_med * 1e-6) / 1e12, 1)},
+            "backward": {"us": round(bwd_med, 2), "TFLOP/s": round(bwd_flops(M, n, m, r) / (bwd_med * 1e-6) / 1e12, 1)},
+        }
 
     out = {
         "metric": "QLoRA linear fwd+bwd TFLOP/s and NF4 weight GB/s (% of roofline), 1 MI355X",
@@ -191,8 +304,12 @@ def main():
         "quantize": quant,
         "kernels": other,
     }
-    if not args.no_cpu_baseline:
+    out.update(extra)
+    if not args.no_extra:
         del W, x, g, A, B, h, gx, ws_f, ws_b
+        torch.cuda.empty_cache()
+        out["small_tokens"] = small_token_block(Q, dev, 10)
+    if not args.no_cpu_baseline:
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -118,7 +118,46 @@ def linear_fwd(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Te
     return h, u
 
 
-def linear_fwd_grouped(layers, workspace: torch.Tensor | None = None):
+class GroupedForward:
+    """A reusable grouped forward: outputs, descriptors and workspace are made once.
+
+    layers: sequence of (x, q, A, B, s) as for linear_fwd, all with the same
+    token count M.  run() launches the forward of every layer (one launch
+    pair for M <= 32) and returns the list of (h, u) output tensors.
+    """
+
+    def __init__(self, layers):
+        if not layers:
+            raise ValueError("no layers")
+        self.M = layers[0][0].shape[0]
+        self.device = layers[0][0].device
+        self.keep = list(layers)
+        self.descs = (_lib.LinearLayer * len(layers))()
+        self.outs = []
+        for i, (x, q, A, B, s) in enumerate(layers):
+            r = A.shape[0]
+            _need(x, torch.bfloat16, (self.M, q.n), "x")
+            _need(A, torch.bfloat16, (r, q.n), "A")
+            _need(B, torch.bfloat16, (q.m, r), "B")
+            h = torch.empty((self.M, q.m), dtype=torch.bfloat16, device=self.device)
+            u = torch.empty((self.M, r), dtype=torch.float32, device=self.device)
+            self.outs.append((h, u))
+            self.descs[i] = _lib.LinearLayer(q.n, q.m, r, float(s), x.data_ptr(), q.codes.data_ptr(),
+                                             q.absmax8.data_ptr(), q.c2.data_ptr(), A.data_ptr(), B.data_ptr(),
+                                             h.data_ptr(), u.data_ptr())
+        need = _lib.load().qlora_grouped_workspace_bytes(self.M, len(layers), self.descs)
+        if need == 0:
+            raise ValueError("invalid grouped forward arguments")
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def run(self):
+        st = _lib.load().qlora_linear_fwd_grouped(self.M, len(self.keep), self.descs, _ptr(self.workspace),
+                                                  self.workspace.numel(), _stream(self.device))
+        _lib.check(st, "qlora_linear_fwd_grouped")
+        return self.outs
+
+
+def linear_fwd_grouped(layers):
     """Forward of several layers sharing the token count M, in one call.
 
     layers: sequence of (x, q, A, B, s) as for linear_fwd.  Returns a list of
@@ -126,29 +165,7 @@ def linear_fwd_grouped(layers, workspace: torch.Tensor | None = None):
     """
     if not layers:
         return []
-    M = layers[0][0].shape[0]
-    dev = layers[0][0].device
-    descs = (_lib.LinearLayer * len(layers))()
-    outs = []
-    for i, (x, q, A, B, s) in enumerate(layers):
-        r = A.shape[0]
-        _need(x, torch.bfloat16, (M, q.n), "x")
-        _need(A, torch.bfloat16, (r, q.n), "A")
-        _need(B, torch.bfloat16, (q.m, r), "B")
-        h = torch.empty((M, q.m), dtype=torch.bfloat16, device=dev)
-        u = torch.empty((M, r), dtype=torch.float32, device=dev)
-        outs.append((h, u))
-        descs[i] = _lib.LinearLayer(q.n, q.m, r, float(s), x.data_ptr(), q.codes.data_ptr(), q.absmax8.data_ptr(),
-                                    q.c2.data_ptr(), A.data_ptr(), B.data_ptr(), h.data_ptr(), u.data_ptr())
-    lib = _lib.load()
-    need = lib.qlora_grouped_workspace_bytes(M, len(layers), descs)
-    if need == 0:
-        raise ValueError("invalid grouped forward arguments")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib.qlora_linear_fwd_grouped(M, len(layers), descs, _ptr(workspace), workspace.numel(), _stream(dev))
-    _lib.check(st, "qlora_linear_fwd_grouped")
-    return outs
+    return GroupedForward(layers).run()
 
 
 def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
