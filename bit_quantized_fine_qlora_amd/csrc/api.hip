@@ -1,6 +1,8 @@
 // C ABI of the QLoRA adapted-linear library: argument checks, workspace
 // layout, kernel dispatch and optional kernel timing.  Declared in qlora.h.
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -73,6 +75,19 @@ Nf4Table build_table() {
   // exact symmetry of the construction, kept exact after rounding
   for (int j = 0; j < 8; ++j) t.q[j] = -t.q[15 - j];
   for (int j = 0; j < 15; ++j) t.t[j] = (float)(((double)t.q[j] + (double)t.q[j + 1]) * 0.5);
+  // The quantizer finds the code of |w/c1| through a table of eighth-binade
+  // intervals of [2^-4, 1] that may hold at most one positive threshold each
+  // (and none below 2^-4); these thresholds satisfy that, checked here once.
+  uint32_t prev = 0;
+  for (int j = 8; j < 15; ++j) {
+    uint32_t b;
+    std::memcpy(&b, &t.t[j], 4);
+    if (b < 0x3D800000u || (j > 8 && (b >> 20) == (prev >> 20))) {
+      std::fprintf(stderr, "qlora: NF4 threshold layout breaks the quantizer's interval table\n");
+      std::abort();
+    }
+    prev = b;
+  }
   return t;
 }
 

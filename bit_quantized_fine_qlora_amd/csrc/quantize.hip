@@ -10,16 +10,14 @@
 namespace qlora {
 
 // fl32(w / c) for |w| <= c, c in [2^-100, 2^100], |w| >= 2^-100, with y the
-// correctly rounded 1/c.  Two fused multiply-add corrections of w*y; the
-// second one starts from a quotient within one ulp, where the remainder
-// w - c*q is exact and one more step rounds correctly (Markstein's
-// reciprocal-based division theorem).
+// correctly rounded 1/c.  q0 = RN(w y) is within one ulp of w / c, the
+// remainder w - c q0 is exact (one fused multiply-add), and one more fused
+// step RN(q0 + r y) is the correctly rounded quotient (Markstein's theorem
+// for reciprocal-based division).
 __device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) {
   const float q0 = w * y;
   const float r0 = __builtin_fmaf(-c, q0, w);
-  const float q1 = __builtin_fmaf(r0, y, q0);
-  const float r1 = __builtin_fmaf(-c, q1, w);
-  return __builtin_fmaf(r1, y, q1);
+  return __builtin_fmaf(r0, y, q0);
 }
 
 // Stored code of the level nearest to v: the level index is the number of
@@ -29,14 +27,27 @@ __device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) 
 //   v > 0 : level 8 + #{T_j < v}        -> code #{T_j < |v|}
 //   v <= 0: level 7 - #{T_j <= |v|}     -> code 8 + #{T_j < succ(|v|)}
 // (succ(|v|) is |v|'s bit pattern + 1; -0 and +0 both give level 7).
-__device__ __forceinline__ uint32_t nf4_code(float v, const uint32_t (&tb)[7]) {
+//
+// The count uses a 33-entry table over |v| in [2^-4, 1]: entry i covers the
+// bit patterns [2^-4 bits + i * 2^20, + 2^20) (an eighth of a binade) and
+// holds the number of thresholds below its start and the one threshold
+// inside it, if any (no interval holds two; the host-side table build checks
+// this).  |v| < 2^-4 lies below every threshold (entry 0 is empty) and
+// |v| = 1 is entry 32.  The key succ(|v|) may fall in the next interval, but
+// only at its very first pattern, which no threshold of the current entry
+// can reach, so base + [key > thr] is still the count.
+constexpr int kCodeLutSize = 33;
+constexpr uint32_t kCodeLutLo = 0x3D800000u;   // bit pattern of 2^-4
+
+__device__ __forceinline__ uint32_t nf4_code(float v, const uint2* lut) {
   const uint32_t bits = __float_as_uint(v);
+  const uint32_t abits = bits & 0x7FFFFFFFu;
   const uint32_t neg = ((int32_t)bits <= 0) ? 1u : 0u;
-  const uint32_t key = (bits & 0x7FFFFFFFu) + neg;
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) m += (key > tb[j]) ? 1u : 0u;
-  return m | (neg << 3);
+  const uint32_t key = abits + neg;
+  int idx = (int)(abits >> 20) - (int)(kCodeLutLo >> 20);
+  idx = idx < 0 ? 0 : (idx > kCodeLutSize - 1 ? kCodeLutSize - 1 : idx);
+  const uint2 e = lut[idx];
+  return (e.x + (key > e.y ? 1u : 0u)) | (neg << 3);
 }
 
 // One workgroup per double-quant group (256 blocks of 64 weights).  In each
@@ -48,12 +59,23 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
                                                                float* __restrict__ c2out, Nf4Table tab) {
   __shared__ float s_c1[kGroupBlocks];
   __shared__ float s_red[4];
+  __shared__ uint2 s_lut[kCodeLutSize];
   const int tid = threadIdx.x;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
   const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
-  uint32_t tb[7];  // bit patterns of the positive thresholds T_8..T_14
+  if (tid < kCodeLutSize) {
+    const uint32_t lo = kCodeLutLo + ((uint32_t)tid << 20);
+    const uint32_t hi = lo + (1u << 20);
+    uint32_t below = 0, inside = 0xFFFFFFFFu;
 #pragma unroll
-  for (int j = 0; j < 7; ++j) tb[j] = __float_as_uint(tab.t[8 + j]);
+    for (int j = 0; j < 7; ++j) {
+      const uint32_t t = __float_as_uint(tab.t[8 + j]);
+      below += t < lo ? 1u : 0u;
+      if (t >= lo && t < hi) inside = t;
+    }
+    s_lut[tid] = make_uint2(below, inside);
+  }
+  __syncthreads();
 
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
@@ -82,9 +104,10 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
 
     // Fast path needs every quotient away from underflow; anything else
     // (zeros, tiny or huge constants) takes the IEEE division.
-    bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f);
+    float amin = fabsf(w[0]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) slow |= fabsf(w[i]) < 0x1p-100f;
+    for (int i = 1; i < 16; ++i) amin = fminf(amin, fabsf(w[i]));
+    const bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f) || !(amin >= 0x1p-100f);
     float q[16];
     if (!slow) {
       const float y = 1.0f / c1;
@@ -98,8 +121,8 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lo |= (nf4_code(q[j], tb) | (nf4_code(q[j + 4], tb) << 4)) << (8 * j);
-      hi |= (nf4_code(q[8 + j], tb) | (nf4_code(q[12 + j], tb) << 4)) << (8 * j);
+      lo |= (nf4_code(q[j], s_lut) | (nf4_code(q[j + 4], s_lut) << 4)) << (8 * j);
+      hi |= (nf4_code(q[8 + j], s_lut) | (nf4_code(q[12 + j], s_lut) << 4)) << (8 * j);
     }
     if (valid) {
       u32x2 pk = {lo, hi};

@@ -1,8 +1,8 @@
 """CPU check of the quantizer kernel's division step.
 
-The kernel computes fl32(w / c1) as two fused multiply-add corrections of
-w * RN(1/c1) (its fast path, used when |w| >= 2^-100 and c1 in [2^-100,
-2^100]).  The snippet below restates that arithmetic in C (gcc, IEEE fmaf)
+The kernel computes fl32(w / c1) as one fused multiply-add correction of
+w * RN(1/c1) (Markstein's reciprocal-based division; its fast path, used when
+|w| >= 2^-100 and c1 in [2^-100, 2^100]).  The snippet below restates that arithmetic in C (gcc, IEEE fmaf)
 and checks it against the correctly rounded quotient on random pairs, on
 quotients placed exactly at, and one ulp around, every NF4 threshold, and
 on worst-case-looking significands.  It shares nothing with the oracle.
@@ -23,9 +23,7 @@ C_SRC = r"""
 static float fast_div(float w, float c, float y) {
   float q0 = w * y;
   float r0 = fmaf(-c, q0, w);
-  float q1 = fmaf(r0, y, q0);
-  float r1 = fmaf(-c, q1, w);
-  return fmaf(r1, y, q1);
+  return fmaf(r0, y, q0);
 }
 static uint64_t st = 88172645463325252ull;
 static uint32_t rnd(void) { st ^= st << 13; st ^= st >> 7; st ^= st << 17; return (uint32_t)(st >> 16); }
