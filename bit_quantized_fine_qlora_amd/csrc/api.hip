@@ -22,7 +22,7 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
                      float s, const Nf4Table& tab, hipStream_t stream);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
-                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
+                       const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream);
 int small_max_tokens();
 int small_max_layers();
@@ -194,7 +194,7 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t At, Bt, part_uv, u, v, gA, gB, gpad, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, total;
   int su, sv, sa, sb;
   int64_t m_pad;  // row length of g as the kernels read it
 };
@@ -211,7 +211,6 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   w.sv = down_proj_splits(M, w.m_pad, r);
   w.sa = token_grad_splits(M, n, r);
   w.sb = token_grad_splits(M, w.m_pad, r);
-  w.At = L.take((size_t)n * r * 2);
   w.Bt = L.take((size_t)w.m_pad * r * 2);
   const int suv = w.su > w.sv ? w.su : w.sv;
   w.part_uv = L.take((size_t)suv * M * r * sizeof(float));
@@ -415,7 +414,6 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
     uu = at<float>(workspace, w.u);
   }
   uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
-  uint16_t* At = at<uint16_t>(workspace, w.At);
   float* v = at<float>(workspace, w.v);
   {
     Timed tm("transpose", hs);
@@ -434,12 +432,8 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
     launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
   }
   if (grad_x) {
-    {
-      Timed tm("transpose", hs);
-      launch_transpose_bf16(A, r, n, r, At, hs);
-    }
     Timed tm("dgrad_gemm", hs);
-    launch_dgrad_gemm(gk, codes, absmax8, c2, At, v, grad_x, M, n, m, w.m_pad, r, s, table(), hs);
+    launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, table(), hs);
   }
   return hip_status();
 }

@@ -8,23 +8,29 @@
 // scaled adapter branch).
 //
 // gfx950 design, from measurements on the device:
-//   - the matrix pipe stays busy while a SIMD issues at most ~2 VALU ops per
-//     16x16x32 MFMA; dequantization costs ~3 VALU ops per weight, so each
-//     dequantized weight must feed >= 256 tokens;
-//   - activation rows must be read as whole 128-byte lines (scattered 16-byte
-//     fragment loads reach only ~15 B/clk/CU from L2, line-coalesced loads
-//     ~45 B/clk/CU);
-//   - LDS reads reach ~210 B/clk/CU with two waves per SIMD.
-// So a workgroup of 8 waves (2 per SIMD) covers 256 output features x 256
-// tokens.  Per K step (64): the activation tile (256 x 64) is loaded with
-// line-coalesced 16-byte loads and stored to LDS; waves 0-3 dequantize the
-// 256 x 64 W' tile (one 64-weight block per thread, one magnitude table per
-// block) into LDS, so each SIMD pairs a dequantizing wave with an MFMA-only
-// wave; every wave then runs 64 MFMAs on its 128 x 64 output tile from LDS
-// fragments.  The forward reads W' with ds_read_b128; the backward contracts
-// over W0's rows, so it reads the natural-layout tile transposed with
-// ds_read_b64_tr_b16.  LDS layouts are XOR-swizzled to avoid bank conflicts.
-// Two LDS stages of {W' 32 KB, activations 32 KB}: 128 KB.
+//   - a wave that mixes VALU work with its own MFMAs serializes the two, but
+//     VALU work of another wave on the same SIMD runs under that SIMD's
+//     MFMAs; so dequantization and the activation copy go to waves of their
+//     own, and the MFMA waves only read LDS fragments and issue MFMAs;
+//   - dequantization costs ~3 VALU ops per weight, so each dequantized weight
+//     must feed >= 256 tokens;
+//   - activation rows are read as whole 128-byte lines (scattered 16-byte
+//     fragment loads reach only a third of the rate from L2).
+// A workgroup of 12 waves covers 256 output features x 256 tokens: 8 MFMA
+// waves (2 per SIMD, each a 128 x 64 output tile) and 4 producer waves (one
+// per SIMD).  Per K step (64) the producers store the dequantized W' tile
+// (256 x 64, one 64-weight block per thread, one magnitude table per block)
+// of the next step into the other LDS stage and issue the code loads of the
+// step after, while the MFMA waves run 64 MFMAs each on the current stage;
+// the MFMA waves also start the copy of the next activation tile (256 x 64)
+// with buffer loads that write LDS directly (no registers, 4 per wave).  The forward reads W' with
+// ds_read_b128; the backward contracts over W0's rows, so it reads the
+// natural-layout tile transposed with ds_read_b64_tr_b16.  LDS rows are
+// padded (pitches below) so that every store and fragment read is free of
+// bank conflicts and every fragment address is one per-lane base plus an
+// immediate offset.  Two LDS stages of {W', activations}: 134-136 KB.  The
+// LoRA term runs as extra K steps whose tiles the producers fill from the
+// adapter factors.
 #include "qlora_common.h"
 
 namespace qlora {
@@ -33,10 +39,35 @@ namespace lg2 {
 constexpr int BF = 256;              // output features per tile
 constexpr int BT = 256;              // tokens per tile
 constexpr int BK = 64;               // K per step
-constexpr int WTILEB = BF * BK * 2;  // 32 KB
-constexpr int ATILEB = BT * BK * 2;  // 32 KB
-constexpr int STAGEB = WTILEB + ATILEB;
-constexpr int LDSB = 2 * STAGEB;     // 128 KB
+// LDS row pitches.  Measured bank rules: a ds_write_b128 serves 8 lanes per
+// cycle, conflict-free when their 16-byte slots differ in address bits 4-6;
+// a ds_read_b128 serves 16 lanes, conflict-free when bits 4-7 differ; a
+// ds_read_b64_tr_b16 serves 16 lanes (4 rows x 32 bytes), conflict-free when
+// the four 32-byte runs do not overlap modulo 256 bytes.
+//   forward W' [256 rows][64 K] bf16: pitch 144 = 9 x 16, so 8 or 16
+//     consecutive rows at one chunk fall on distinct slots.
+//   activations [256 rows][64 K] bf16: pitch 128, written 1 KB (8 rows) at a
+//     time by the direct-to-LDS loads, so the 16-byte chunk c of row r sits
+//     at position c ^ (r & 7) instead (the loads pick their sources to match).
+//   backward W' [64 K rows][256 features]: pitch 560 = 35 x 16; a dequant
+//     store (8 consecutive rows, one chunk) hits slots 3r + d mod 8, and the
+//     4 consecutive rows of a transposed read start 48 bytes apart.
+constexpr int AP = 144;
+constexpr int WPB = 560;
+constexpr int ATILEB = BT * 128;     // 32 KB
+template <bool kBwd> struct Tile {
+  static constexpr int W = kBwd ? BK * WPB : BF * AP;  // 35 / 36 KB
+};
+// The four LDS tiles are separate arrays (136 KB in all): the compiler then
+// knows that reading one stage does not alias the direct-to-LDS copy into
+// the other, and does not make the reads wait for that copy.  Stage indices
+// are compile-time constants (the K loops are unrolled by two).
+struct Lds {
+  uint8_t* w[2];
+  uint8_t* a[2];
+};
+constexpr int kMfmaWaves = 8;
+constexpr int kThreads = 64 * (kMfmaWaves + 4);
 }  // namespace lg2
 
 struct GemmArgs {
@@ -44,7 +75,7 @@ struct GemmArgs {
   const uint8_t* codes;    // quantized W0, m x n
   const uint8_t* absmax8;
   const float* c2;
-  const uint16_t* lora_a;  // N x r: B (forward) or A^T (backward)
+  const uint16_t* lora_a;  // B (m x r, forward) or A (r x n, backward)
   const float* lora_b;     // M x r: u (forward) or v (backward)
   uint16_t* out;           // M x N
   int64_t M, K, N;         // tokens, contraction, output features
@@ -61,71 +92,187 @@ __device__ __forceinline__ int xcd_remap_l(int bid, int nblocks) {
   return (bid & 7) * (nblocks >> 3) + (bid >> 3);
 }
 
-// [rows][64] bf16 tile (activations; forward W'): 16-byte chunk c of row r at
-// chunk position c ^ (r & 7).
-__device__ __forceinline__ uint32_t sw64(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
-}
-// Backward W' tile [64 K-rows][256 features] bf16: 32-byte chunk c (16
-// features) of row r at chunk position c ^ sw(r), sw(r) = (r & 3) |
-// ((r >> 3) & 1) << 2, which spreads the 16 rows of one transposed read
-// (8q + 4h + 0..3 for the four lane groups q) over all bank groups.
-__device__ __forceinline__ uint32_t swbwd(int row, int col) {
-  const int sw = (row & 3) | (((row >> 3) & 1) << 2);
-  return (uint32_t)(row * 512 + ((((col >> 4) ^ sw)) << 5) + ((col & 15) << 1));
-}
-
+// Producer waves (256 threads, pt = 0..255): activation tile copy, W' tile
+// dequantization, and the LoRA epilogue operands.
 template <bool kBwd>
-__global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table tab) {
-  __shared__ __align__(16) uint8_t smem[lg2::LDSB];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lr = lane & 15;
-  const int lq = lane >> 4;
-  const int bid = xcd_remap_l(blockIdx.x, gridDim.x);
-  const int tile_f = bid % p.tiles_f;
-  const int tile_t = bid / p.tiles_f;
-  const int64_t f0 = (int64_t)tile_f * lg2::BF;
-  const int64_t t0 = (int64_t)tile_t * lg2::BT;
+__device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table& tab, const lg2::Lds& lds, int pt,
+                                              int64_t f0, int64_t t0, int nk) {
   const int64_t K = p.K;
-  const int nk = (int)((K + lg2::BK - 1) / lg2::BK);
   const int64_t wn = p.wn;
   const int64_t wnumel = p.wm * wn;
-  const int wf = (wave & 1) * 128;  // this wave's 128 output features in the tile
-  const int wt = (wave >> 1) * 64;  // this wave's 64 tokens
-
   // Buffer resources: reads past a tensor's end return 0.  Rows past M (or
   // past m / n of W0) read zeros or other rows of the same tensor; they only
   // feed outputs that are never stored.  In the backward's last K step the
   // W0 rows past m read zero codes and a zero 8-bit constant, i.e. zero
   // weights, so the finite activations there add nothing.
-  const brsrc_t r_act = make_rsrc(p.act, (uint32_t)(p.M * K * 2));
   const brsrc_t r_codes = make_rsrc(p.codes, (uint32_t)(wnumel / 2));
   const brsrc_t r_amax = make_rsrc(p.absmax8, (uint32_t)(wnumel / kBlock));
   const brsrc_t r_c2 = make_rsrc(p.c2, (uint32_t)(((wnumel / kBlock + kGroupBlocks - 1) / kGroupBlocks) * 4));
 
-  // ---- dequant assignment (threads 0..255): one 64-weight block per K step ----
-  // forward : LDS row tid = out feature f0 + tid, block (f0 + tid, ks)
-  // backward: LDS row tid/4 = W0 row 64*ks + tid/4, features f0 + 64*(tid%4) .. +63
-  const int dt = tid & 255;
-  uint32_t c_off, c_step, b_off, b_step;  // byte offsets of codes and absmax8 at step 0, per-step increments
+  // dequant assignment: one 64-weight block per thread and K step
+  // forward : LDS row pt = out feature f0 + pt, block (f0 + pt, ks)
+  // backward: LDS row pt%64 = W0 row 64*ks + pt%64, features f0 + 64*(pt/64) .. +63
+  uint32_t c_off, c_step, b_off, b_step;
   if (!kBwd) {
-    const int64_t e0 = (f0 + dt) * wn;
+    const int64_t e0 = (f0 + pt) * wn;
     c_off = (uint32_t)(e0 / 2);  c_step = lg2::BK / 2;
     b_off = (uint32_t)(e0 / kBlock);  b_step = 1;
   } else {
-    const int64_t e0 = (int64_t)(dt >> 2) * wn + f0 + 64 * (dt & 3);
+    const int64_t e0 = (int64_t)(pt & 63) * wn + f0 + 64 * (pt >> 6);
     c_off = (uint32_t)(e0 / 2);  c_step = (uint32_t)(lg2::BK * wn / 2);
     b_off = (uint32_t)(e0 / kBlock);  b_step = (uint32_t)(lg2::BK * wn / kBlock);
   }
-
-  // ---- activation tile loads: chunk id = i*512 + tid -> row id/8, chunk id%8 ----
-  const int a_row0 = tid >> 3;  // + 64*i
-  const int a_c = tid & 7;
-  uint32_t a_off[4];
+  // Two register sets, so the code loads of step ks + 2 are issued a whole
+  // K step before their data is dequantized.
+  struct Regs {
+    u32x4 code[2];  // 64 codes
+    uint8_t aa;     // absmax8 byte (kept 8-bit so its zero-extension is
+                    // placed at the use, not right after the load)
+    float sa;       // c2 of the group
+  };
+  using T = lg2::Tile<kBwd>;
+  const uint32_t w_st = kBwd ? (uint32_t)((pt & 63) * lg2::WPB + 128 * (pt >> 6)) : (uint32_t)(pt * lg2::AP);
+  auto load = [&](Regs& R) {
+    R.code[0] = bload128(r_codes, c_off);
+    R.code[1] = bload128(r_codes, c_off + 16);
+    R.aa = __builtin_amdgcn_raw_buffer_load_b8(r_amax, (int)b_off, 0, 0);
+    R.sa = __uint_as_float(bload32(r_c2, (b_off >> 8) << 2));
+    c_off += c_step;
+    b_off += b_step;
+  };
+  auto store = [&](const Regs& R, uint8_t* tile) {
+    uint8_t* dW = tile + w_st;
+    const MagLut L = make_mag_lut(tab, e4m3_decode((uint32_t)R.aa) * R.sa);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (uint32_t)(((t0 + 64 * i + a_row0) * K + 8 * a_c) * 2);
+    for (int d = 0; d < 8; ++d) {
+      uint32_t o[4];
+      mag_dequant8(L, R.code[d >> 2][d & 3], o);
+      *reinterpret_cast<u32x4*>(dW + 16 * d) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  };
+  // K step ks: `cur` holds step ks + 1, `nxt` receives step ks + 2.  The
+  // loads are unconditional (past the end they read other rows or zeros and
+  // are never stored), which keeps the compiler's wait counts exact: a
+  // conditional load makes it wait for the prefetch just issued.
+  auto step = [&](Regs& cur, Regs& nxt, uint8_t* next_tile) {
+    load(nxt);
+    store(cur, next_tile);
+    __syncthreads();
+  };
+  (void)K;
+
+  // The LoRA term s * lora_b lora_a^T runs as nq = ceil(r / 32) extra K
+  // steps of 64 that the producers fill: step q pairs ranks 32q .. 32q + 31
+  // twice, once with the bf16 hi part of s * lora_b and once with its lo part
+  // (the fp32 factor as hi + lo; lora_a is bf16 already).
+  //   forward : W' row f (feature), k: B[f][32q + k % 32]
+  //   backward: W' row k, feature f:   A[32q + k % 32][f]
+  //   activations row t, k < 32: hi(s u[t][32q + k]), k >= 32: lo(s u[t][32q + k - 32])
+  //   (v instead of u in the backward)
+  // Out-of-range rows, features and ranks are zero.  The operands of q = 0
+  // are loaded in the prologue and stay in registers through the K loop.
+  const int r = p.r;
+  const int nq = (r + 31) / 32;
+  struct LoraRegs {
+    u32x4 f[kBwd ? 8 : 4];
+    float t[32];
+  };
+  LoraRegs LR;
+  auto lora_load = [&](int q) {
+    const int q0 = 32 * q;
+    if (!kBwd) {
+      const int64_t f = f0 + pt;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int qb = q0 + 8 * c;
+        if (f < p.N && (r & 7) == 0 && qb + 8 <= r) {
+          LR.f[c] = *reinterpret_cast<const u32x4*>(p.lora_a + f * r + qb);
+        } else {
+          uint32_t v[4] = {0u, 0u, 0u, 0u};
+          if (f < p.N)
+            for (int e = 0; e < 8; ++e)
+              if (qb + e < r) v[e >> 1] |= (uint32_t)p.lora_a[f * r + qb + e] << (16 * (e & 1));
+          LR.f[c] = u32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    } else {
+      const int rank = q0 + (pt & 31);
+      const int64_t fb = f0 + 64 * (pt >> 6);  // n % 64 == 0: all 64 features in range or none
+      const bool ok = rank < r && fb < p.N;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        LR.f[c] = ok ? *reinterpret_cast<const u32x4*>(p.lora_a + (int64_t)rank * p.N + fb + 8 * c)
+                     : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int64_t t = t0 + pt;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int qb = q0 + 4 * c;
+      if (t < p.M && (r & 3) == 0 && qb + 4 <= r) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p.lora_b + t * r + qb);
+        LR.t[4 * c] = v[0]; LR.t[4 * c + 1] = v[1]; LR.t[4 * c + 2] = v[2]; LR.t[4 * c + 3] = v[3];
+      } else {
+        for (int e = 0; e < 4; ++e) LR.t[4 * c + e] = (t < p.M && qb + e < r) ? p.lora_b[t * r + qb + e] : 0.0f;
+      }
+    }
+  };
+  auto lora_store = [&](uint8_t* wtile, uint8_t* atile) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const u32x4 v = kBwd ? LR.f[d] : LR.f[d & 3];
+      *reinterpret_cast<u32x4*>(wtile + w_st + 16 * d) = v;
+    }
+    // activation row pt: chunk c at position c ^ (pt % 8)
+    uint8_t* arow = atile + pt * 128;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float h0, l0, h1, l1;
+        split_bf16(p.s * LR.t[8 * c + 2 * e], h0, l0);
+        split_bf16(p.s * LR.t[8 * c + 2 * e + 1], h1, l1);
+        hi[e] = pack_bf16x2(h0, h1);
+        lo[e] = pack_bf16x2(l0, l1);
+      }
+      *reinterpret_cast<u32x4*>(arow + ((c ^ (pt & 7)) << 4)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(arow + (((c + 4) ^ (pt & 7)) << 4)) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+  };
+
+  Regs R0, R1;
+  // prologue: stage 0 <- step 0, R1 <- step 1, LoRA operands of q = 0
+  load(R0);
+  load(R1);
+  if (nq > 0) lora_load(0);
+  store(R0, lds.w[0]);
+  __syncthreads();
+  // K step ks stores step ks + 1 into stage (ks + 1) % 2: regular steps 1 .. nk - 1
+#pragma unroll 1
+  for (int ks = 0; ks < nk - 1; ks += 2) {
+    step(R1, R0, lds.w[1]);
+    if (ks + 1 < nk - 1) step(R0, R1, lds.w[0]);
+  }
+  // LoRA steps nk .. nk + nq - 1, then the last step's barrier
+  for (int q = 0; q < nq; ++q) {
+    const int j = nk + q;
+    lora_store((j & 1) ? lds.w[1] : lds.w[0], (j & 1) ? lds.a[1] : lds.a[0]);
+    if (q + 1 < nq) lora_load(q + 1);
+    __syncthreads();
+  }
+  __syncthreads();
+}
+
+// MFMA waves (512 threads): each owns a 128-feature x 64-token output tile.
+template <bool kBwd>
+__device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds& lds, int tid, int64_t f0,
+                                              int64_t t0, int nk) {
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int wf = (wave & 1) * 128;
+  const int wt = (wave >> 1) * 64;
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -133,173 +280,145 @@ __global__ __launch_bounds__(512) void linear_gemm_kernel(GemmArgs p, Nf4Table t
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[4];        // activation chunks of the next K step
-  u32x4 creg[2];        // 64 codes of the next dequant step
-  uint32_t aa = 0;      // absmax8 byte
-  float sa = 0.f;       // c2 of the group
+  using T = lg2::Tile<kBwd>;
+  // Activation tile copy: this wave fills rows 32 w .. 32 w + 31 of the tile,
+  // 8 rows (1 KB) per load; lane l lands at byte 16 l of its block, i.e. row
+  // l / 8, chunk position l % 8, which holds chunk (l % 8) ^ (l / 8).  Rows
+  // past M are out of the buffer's range and read 0.
+  const brsrc_t r_act = make_rsrc(p.act, (uint32_t)(p.M * p.K * 2));
+  uint32_t act_off = (uint32_t)(((t0 + 32 * wave + (lane >> 3)) * p.K + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  const uint32_t act_blk = (uint32_t)(8 * p.K * 2);
+  auto copy_act = [&](uint8_t* tile) {
+    uint8_t* dst = tile + 32 * 128 * wave;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16,
+                                               act_off + act_blk * b, 0, 0, 0);
+    act_off += lg2::BK * 2;
+  };
 
-  auto load_act = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      areg[i] = bload128(r_act, a_off[i]);
-      a_off[i] += lg2::BK * 2;
+  // Fragment addresses: one per-lane base plus immediate offsets.
+  //   activations: row wt + 16 j + lr, chunk 4 kk + lq at position (4 kk + lq) ^ (lr % 8)
+  //   forward W' : row wf + 16 i + lr, chunk 4 kk + lq
+  //   backward W': K rows 32 kk + 8 lq + 4 h + lr/4, features wf + 16 i + 4 (lr % 4) .. +3
+  const uint32_t a_base0 = (uint32_t)((wt + lr) * 128 + ((lq ^ (lr & 7)) << 4));
+  const uint32_t a_base1 = a_base0 ^ 64u;
+  const uint32_t w_base = kBwd ? (uint32_t)((8 * lq + (lr >> 2)) * lg2::WPB + 2 * (wf + 4 * (lr & 3)))
+                               : (uint32_t)((wf + lr) * lg2::AP + 16 * lq);
+  // A fragment i of step kk
+  auto load_a = [&](const uint8_t* sW, int kk, int i) -> u32x4 {
+    if (!kBwd) {
+      return *reinterpret_cast<const u32x4*>(sW + w_base + 64 * kk + 16 * lg2::AP * i);
+    } else {
+      const uint8_t* src = sW + w_base + 32 * lg2::WPB * kk + 32 * i;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 4 * lg2::WPB));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
     }
   };
-  auto store_act = [&](int stage) {
-    uint8_t* dA = smem + stage * lg2::STAGEB + lg2::WTILEB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dA + sw64(64 * i + a_row0, a_c)) = areg[i];
-  };
-  auto load_w = [&]() {
-    creg[0] = bload128(r_codes, c_off);
-    creg[1] = bload128(r_codes, c_off + 16);
-    aa = bload8(r_amax, b_off);
-    sa = __uint_as_float(bload32(r_c2, (b_off >> 8) << 2));
-    c_off += c_step;
-    b_off += b_step;
-  };
-  auto dequant_store = [&](int stage) {
-    uint8_t* dW = smem + stage * lg2::STAGEB;
-    const MagLut L = make_mag_lut(tab, e4m3_decode(aa) * sa);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t o[4];
-      mag_dequant8(L, creg[d >> 2][d & 3], o);
-      const uint32_t off = kBwd ? swbwd(dt >> 2, 64 * (dt & 3) + 8 * d) : sw64(dt, d);
-      *reinterpret_cast<u32x4*>(dW + off) = u32x4{o[0], o[1], o[2], o[3]};
-    }
-  };
-  auto mfma_step = [&](int stage, int kk) {
-    const uint8_t* sW = smem + stage * lg2::STAGEB;
-    const uint8_t* sA = sW + lg2::WTILEB;
+  // 32 MFMAs of one K = 32 half step.  A fragments are software-pipelined one
+  // ahead; the scheduling barriers keep the compiler from hoisting all eight
+  // (the accumulators leave room for two).
+  auto mfma_step = [&](const uint8_t* sW, const uint8_t* sA, int kk) {
     u32x4 b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4*>(sA + sw64(wt + 16 * j + lr, 4 * kk + lq));
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(sA + (kk ? a_base1 : a_base0) + 2048 * j);
+    u32x4 a_cur = load_a(sW, kk, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      u32x4 a;
-      if (!kBwd) {
-        a = *reinterpret_cast<const u32x4*>(sW + sw64(wf + 16 * i + lr, 4 * kk + lq));
-      } else {
-        // K rows 32*kk + 8*lq + 4*h + lr/4, feature columns wf + 16*i + 4*(lr%4) .. +3
-        const int row = 32 * kk + 8 * lq + (lr >> 2);
-        const int col = wf + 16 * i + 4 * (lr & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sW + swbwd(row, col)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sW + swbwd(row + 4, col)));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        a = u32x4{l2[0], l2[1], h2[0], h2[1]};
-      }
+      u32x4 a_nxt;
+      if (i < 7) a_nxt = load_a(sW, kk, i + 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a, b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a_cur, b[j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < 7) a_cur = a_nxt;
     }
   };
-  // One K step on LDS stage `stage`: the registers holding step ks+1 go to
-  // the other stage (activations stored, W' dequantized by waves 0-3) while
-  // the MFMAs run, and the loads of step ks+2 are issued.
-  auto step_dq = [&](int stage) {
-    store_act(stage ^ 1);
-    load_act();
-    mfma_step(stage, 0);
-    dequant_store(stage ^ 1);
-    load_w();
-    mfma_step(stage, 1);
+
+  // s_waitcnt vmcnt(0): the direct-to-LDS loads of this wave have landed
+  constexpr int kWaitVm0 = 0x0F70;
+  // K step ks on stage (w, a) while the next activation tile goes to a_next
+  auto step = [&](int ks, const uint8_t* w, const uint8_t* a, uint8_t* a_next) {
+    if (ks + 1 < nk) copy_act(a_next);
+    mfma_step(w, a, 0);
+    mfma_step(w, a, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-  auto step_mm = [&](int stage) {
-    store_act(stage ^ 1);
-    load_act();
-    mfma_step(stage, 0);
-    mfma_step(stage, 1);
-    __syncthreads();
-  };
-
-  // prologue: stage 0 <- step 0; registers <- step 1
-  const bool dq_wave = wave < 4;
-  load_act();
-  if (dq_wave) load_w();
-  store_act(0);
-  if (dq_wave) {
-    dequant_store(0);
-    load_w();
-  }
-  load_act();
-  __syncthreads();
-
-  if (dq_wave) {
+  // nk steps of W' and activations, then the LoRA steps (filled by the producers)
+  const int nsteps = nk + (p.r + 31) / 32;
+  copy_act(lds.a[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();  // stage 0 ready
 #pragma unroll 1
-    for (int ks = 0; ks < nk; ++ks) step_dq(ks & 1);
-  } else {
-#pragma unroll 1
-    for (int ks = 0; ks < nk; ++ks) step_mm(ks & 1);
+  for (int ks = 0; ks < nsteps; ks += 2) {
+    step(ks, lds.w[0], lds.a[0], lds.a[1]);
+    if (ks + 1 < nsteps) step(ks + 1, lds.w[1], lds.a[1], lds.a[0]);
   }
 
-  // ---- epilogue: + s * lora_b lora_a^T as extra K=32 MFMA steps (fp32 factor split hi + lo) ----
-  const int r = p.r;
-  for (int q0 = 0; q0 < r; q0 += 32) {
-    u32x4 la[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t f = f0 + wf + 16 * i + lr;
-      uint32_t v[4] = {0u, 0u, 0u, 0u};
-      const int qb = q0 + 8 * lq;
-      if (f < p.N) {
-        const uint16_t* src = p.lora_a + f * r + qb;
-        if (qb + 8 <= r && (r & 7) == 0) {
-          const u32x4 t = *reinterpret_cast<const u32x4*>(src);
-          v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (qb + e < r) v[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-        }
-      }
-      la[i] = u32x4{v[0], v[1], v[2], v[3]};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + wt + 16 * j + lr;
-      float bv[8];
-      const int qb = q0 + 8 * lq;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = (t < p.M && qb + e < r) ? p.lora_b[t * r + qb + e] * p.s : 0.0f;
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float h0, l0, h1, l1;
-        split_bf16(bv[2 * e], h0, l0);
-        split_bf16(bv[2 * e + 1], h1, l1);
-        hi[e] = pack_bf16x2(h0, h1);
-        lo[e] = pack_bf16x2(l0, l1);
-      }
-      const u32x4 bh = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      const u32x4 bl = u32x4{lo[0], lo[1], lo[2], lo[3]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[i][j] = mfma16x16x32(la[i], bh, acc[i][j]);
-        acc[i][j] = mfma16x16x32(la[i], bl, acc[i][j]);
-      }
-    }
-  }
-
-  // ---- store (bf16): lane holds 4 consecutive output features of one token ----
-  const bool vec_ok = (p.N & 3) == 0;
+  // ---- store (bf16) through LDS, so that global writes are whole rows ----
+  // The K loop's last barrier has freed all tiles.  Each wave stages its
+  // 64-token x 128-feature tile as [64 rows][256 bytes] in 16 KB of its own
+  // (waves 2w', 2w' + 1 share one 32 KB tile array); 16-byte chunk c of row t
+  // sits at position c ^ (t % 16), so the 8-byte writes (16 rows x 4 lanes)
+  // and the 16-byte row reads are free of bank conflicts.
+  uint8_t* stg = ((wave >> 1) == 0 ? lds.a[0] : (wave >> 1) == 1 ? lds.a[1] : (wave >> 1) == 2 ? lds.w[0] : lds.w[1]) +
+                 16384 * (wave & 1);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t f = f0 + wf + 16 * i + 4 * lq;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + wt + 16 * j + lr;
-      if (t >= p.M) continue;
+      const int row = 16 * j + lr;
+      const int col = 16 * i + 4 * lq;  // 4 features: chunk col / 8, half (col / 4) % 2
       const f32x4 v = acc[i][j];
-      uint16_t* dst = p.out + t * p.N + f;
-      if (vec_ok && f + 3 < p.N) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (f + e < p.N) dst[e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu);
-      }
+      *reinterpret_cast<u32x2*>(stg + row * 256 + ((((col >> 3) ^ (row & 15))) << 4) + ((col & 4) << 1)) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are done
+  __builtin_amdgcn_wave_barrier();
+  const bool vec_ok = (p.N & 7) == 0;
+  const int c = lane & 15;
+  const int64_t f = f0 + wf + 8 * c;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int row = 4 * k + (lane >> 4);
+    const int64_t t = t0 + wt + row;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+    if (t >= p.M || f >= p.N) continue;
+    uint16_t* dst = p.out + t * p.N + f;
+    if (vec_ok && f + 8 <= p.N) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (f + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+template <bool kBwd>
+__global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, Nf4Table tab) {
+  using T = lg2::Tile<kBwd>;
+  __shared__ __align__(16) uint8_t sw0[T::W];
+  __shared__ __align__(16) uint8_t sw1[T::W];
+  __shared__ __align__(16) uint8_t sa0[lg2::ATILEB];
+  __shared__ __align__(16) uint8_t sa1[lg2::ATILEB];
+  const lg2::Lds lds{{sw0, sw1}, {sa0, sa1}};
+  const int tid = threadIdx.x;
+  const int bid = xcd_remap_l(blockIdx.x, gridDim.x);
+  const int tile_f = bid % p.tiles_f;
+  const int tile_t = bid / p.tiles_f;
+  const int64_t f0 = (int64_t)tile_f * lg2::BF;
+  const int64_t t0 = (int64_t)tile_t * lg2::BT;
+  const int nk = (int)((p.K + lg2::BK - 1) / lg2::BK);
+  // wave-uniform split; both roles pass the same number of barriers
+  if (tid >= 64 * lg2::kMfmaWaves)
+    gemm_producer<kBwd>(p, tab, lds, tid - 64 * lg2::kMfmaWaves, f0, t0, nk);
+  else
+    gemm_consumer<kBwd>(p, lds, tid, f0, t0, nk);
 }
 
 static void launch_linear_gemm(bool bwd, const GemmArgs& a, const Nf4Table& tab, hipStream_t stream) {
@@ -308,9 +427,9 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, const Nf4Table& tab,
   p.tiles_t = (int)((p.M + lg2::BT - 1) / lg2::BT);
   const int grid = p.tiles_f * p.tiles_t;
   if (bwd)
-    hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(grid), dim3(512), 0, stream, p, tab);
+    hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
   else
-    hipLaunchKernelGGL(linear_gemm_kernel<false>, dim3(grid), dim3(512), 0, stream, p, tab);
+    hipLaunchKernelGGL(linear_gemm_kernel<false>, dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
 }
 
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
@@ -325,10 +444,10 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 // g is M x m_pad (m_pad = m, or m rounded up to 64 with zero columns when
 // m % 8 != 0, so every 16-byte chunk of the tensor is whole).
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
-                       const uint16_t* At, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
+                       const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream) {
   GemmArgs p{};
-  p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = At; p.lora_b = v; p.out = gx;
+  p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = A; p.lora_b = v; p.out = gx;
   p.M = M; p.K = m_pad; p.N = n; p.wn = n; p.wm = m; p.r = r; p.s = s;
   launch_linear_gemm(true, p, tab, stream);
 }
