@@ -20,10 +20,11 @@ void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c
                     const Nf4Table& tab, hipStream_t stream);
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
-                     float s, const Nf4Table& tab, hipStream_t stream);
+                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream);
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
-                       int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream);
+                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream);
 int small_max_tokens();
 int small_max_layers();
 size_t small_ws_bytes(int64_t M, int64_t n, int64_t m, int r);
@@ -172,8 +173,9 @@ struct WsLayout {
 };
 
 struct FwdWs {
-  size_t part, u, total;
+  size_t part, u, ksplit, total;
   int splits;
+  bool has_ksplit;
 };
 
 FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
@@ -181,7 +183,8 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   FwdWs w;
   if (M <= small_max_tokens()) {  // weight-streaming path: fp32 partials only
     w.splits = 0;
-    w.part = w.u = 0;
+    w.part = w.u = w.ksplit = 0;
+    w.has_ksplit = false;
     L.take(small_ws_bytes(M, n, m, r));
     w.total = L.total;
     return w;
@@ -189,6 +192,9 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   w.splits = down_proj_splits(M, n, r);
   w.part = L.take((size_t)w.splits * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
+  const size_t kb = gemm_split_ws_bytes(M, m, n);  // GEMM tiles split in K
+  w.has_ksplit = kb != 0;
+  w.ksplit = w.has_ksplit ? L.take(kb) : 0;
   w.total = L.total;
   return w;
 }
@@ -318,7 +324,8 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   }
   {
     Timed tm("fwd_gemm", hs);
-    launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s, table(), hs);
+    launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s,
+                    w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs);
   }
   return hip_status();
 }
@@ -433,7 +440,7 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   }
   if (grad_x) {
     Timed tm("dgrad_gemm", hs);
-    launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, table(), hs);
+    launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, nullptr, table(), hs);
   }
   return hip_status();
 }

@@ -85,7 +85,26 @@ struct GemmArgs {
   float s;
   int tiles_f;
   int tiles_t;
+  // Last partial round of tiles split in K (see launch_linear_gemm): work
+  // items full_tiles .. full_tiles + 2 nsplit - 1 are the two K halves of
+  // tiles full_tiles .. full_tiles + nsplit - 1.
+  int full_tiles;
+  int nsplit;
+  float* partial;         // nsplit x 256 x 256 fp32, the first finisher's sum
+  uint32_t* split_sync;   // nsplit x {arrivals, partial ready}, zero at launch
 };
+
+// The two halves of a split tile meet at the end: the first to finish
+// (by an atomic arrival count) stores its fp32 accumulators and raises the
+// ready flag; the second waits for the flag, adds the stored sum to its own
+// and writes the tile.  fp32 addition of two terms is commutative, so the
+// result does not depend on which half finishes first.  The halves may run
+// on different XCDs (separate L2s): every access of the hand-off (sum, count,
+// flag) is device-scope (sc1), which keeps it coherent without acquire /
+// release fences, whose L2 writeback / invalidate would slow every other
+// workgroup on the XCD.
+constexpr uint32_t kSplitSpinLimit = 1u << 22;
+constexpr int kAuxDevice = 16;  // buffer access cache policy: sc1 (device scope)
 
 __device__ __forceinline__ int xcd_remap_l(int bid, int nblocks) {
   if ((nblocks & 7) != 0) return bid;
@@ -96,7 +115,8 @@ __device__ __forceinline__ int xcd_remap_l(int bid, int nblocks) {
 // dequantization, and the LoRA epilogue operands.
 template <bool kBwd>
 __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table& tab, const lg2::Lds& lds, int pt,
-                                              int64_t f0, int64_t t0, int nk) {
+                                              int64_t f0, int64_t t0, int k0, int nk, bool lora, int split,
+                                              uint32_t* lds_word) {
   const int64_t K = p.K;
   const int64_t wn = p.wn;
   const int64_t wnumel = p.wm * wn;
@@ -122,6 +142,8 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
     c_off = (uint32_t)(e0 / 2);  c_step = (uint32_t)(lg2::BK * wn / 2);
     b_off = (uint32_t)(e0 / kBlock);  b_step = (uint32_t)(lg2::BK * wn / kBlock);
   }
+  c_off += (uint32_t)k0 * c_step;  // first K step of this work item
+  b_off += (uint32_t)k0 * b_step;
   // Two register sets, so the code loads of step ks + 2 are issued a whole
   // K step before their data is dequantized.
   struct Regs {
@@ -172,7 +194,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
   // Out-of-range rows, features and ranks are zero.  The operands of q = 0
   // are loaded in the prologue and stay in registers through the K loop.
   const int r = p.r;
-  const int nq = (r + 31) / 32;
+  const int nq = lora ? (r + 31) / 32 : 0;
   struct LoraRegs {
     u32x4 f[kBwd ? 8 : 4];
     float t[32];
@@ -261,24 +283,35 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
     __syncthreads();
   }
   __syncthreads();
+  if (split) {  // the barriers of the split-tile hand-off (see gemm_consumer)
+    __syncthreads();
+    if (*lds_word == 0u) __syncthreads();
+  }
 }
 
-// MFMA waves (512 threads): each owns a 128-feature x 64-token output tile.
+// MFMA waves (512 threads): each owns a WF-feature x WT-token output tile,
+// 128 x 64 in the forward and 64 x 128 in the backward, where the W'
+// fragments come from half-rate transposed reads and the activation
+// fragments from full-rate ones (the 64 x 128 shape halves the former).
 template <bool kBwd>
 __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds& lds, int tid, int64_t f0,
-                                              int64_t t0, int nk) {
+                                              int64_t t0, int k0, int nk, bool lora, int split, uint32_t* lds_word) {
+  constexpr int WF = kBwd ? 64 : 128;
+  constexpr int WT = 128 * 64 / WF;
+  constexpr int NI = WF / 16;  // 16-feature fragments
+  constexpr int NJ = WT / 16;  // 16-token fragments
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps tile offsets scalar
   const int lr = lane & 15;
   const int lq = lane >> 4;
-  const int wf = (wave & 1) * 128;
-  const int wt = (wave >> 1) * 64;
+  const int wf = (wave % (lg2::BF / WF)) * WF;
+  const int wt = (wave / (lg2::BF / WF)) * WT;
 
-  f32x4 acc[8][4];
+  f32x4 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   using T = lg2::Tile<kBwd>;
   // Activation tile copy: this wave fills rows 32 w .. 32 w + 31 of the tile,
@@ -286,7 +319,8 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   // l / 8, chunk position l % 8, which holds chunk (l % 8) ^ (l / 8).  Rows
   // past M are out of the buffer's range and read 0.
   const brsrc_t r_act = make_rsrc(p.act, (uint32_t)(p.M * p.K * 2));
-  uint32_t act_off = (uint32_t)(((t0 + 32 * wave + (lane >> 3)) * p.K + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  uint32_t act_off = (uint32_t)(((t0 + 32 * wave + (lane >> 3)) * p.K + 8 * ((lane & 7) ^ (lane >> 3)) +
+                                  (int64_t)k0 * lg2::BK) * 2);
   const uint32_t act_blk = (uint32_t)(8 * p.K * 2);
   auto copy_act = [&](uint8_t* tile) {
     uint8_t* dst = tile + 32 * 128 * wave;
@@ -318,23 +352,41 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
       return u32x4{l2[0], l2[1], h2[0], h2[1]};
     }
   };
-  // 32 MFMAs of one K = 32 half step.  A fragments are software-pipelined one
-  // ahead; the scheduling barriers keep the compiler from hoisting all eight
-  // (the accumulators leave room for two).
+  auto load_b = [&](const uint8_t* sA, int kk, int j) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(sA + (kk ? a_base1 : a_base0) + 2048 * j);
+  };
+  // 32 MFMAs of one K = 32 half step.  The smaller fragment set is held, the
+  // larger one software-pipelined one ahead; the scheduling barriers keep the
+  // compiler from hoisting all of it (the accumulators leave room for two).
   auto mfma_step = [&](const uint8_t* sW, const uint8_t* sA, int kk) {
-    u32x4 b[4];
+    if constexpr (NI >= NJ) {
+      u32x4 b[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(sA + (kk ? a_base1 : a_base0) + 2048 * j);
-    u32x4 a_cur = load_a(sW, kk, 0);
+      for (int j = 0; j < NJ; ++j) b[j] = load_b(sA, kk, j);
+      u32x4 a_cur = load_a(sW, kk, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 a_nxt;
-      if (i < 7) a_nxt = load_a(sW, kk, i + 1);
+      for (int i = 0; i < NI; ++i) {
+        u32x4 a_nxt;
+        if (i + 1 < NI) a_nxt = load_a(sW, kk, i + 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a_cur, b[j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i < 7) a_cur = a_nxt;
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(a_cur, b[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < NI) a_cur = a_nxt;
+      }
+    } else {
+      u32x4 a[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a[i] = load_a(sW, kk, i);
+      u32x4 b_cur = load_b(sA, kk, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        u32x4 b_nxt;
+        if (j + 1 < NJ) b_nxt = load_b(sA, kk, j + 1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc[i][j] = mfma16x16x32(a[i], b_cur, acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < NJ) b_cur = b_nxt;
+      }
     }
   };
 
@@ -349,7 +401,7 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
     __syncthreads();
   };
   // nk steps of W' and activations, then the LoRA steps (filled by the producers)
-  const int nsteps = nk + (p.r + 31) / 32;
+  const int nsteps = nk + (lora ? (p.r + 31) / 32 : 0);
   copy_act(lds.a[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();  // stage 0 ready
@@ -359,35 +411,85 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
     if (ks + 1 < nsteps) step(ks + 1, lds.w[1], lds.a[1], lds.a[0]);
   }
 
+  // Split tile: arrival order decides who stores its sum and who finishes.
+  // The finisher adds the stored sum through a buffer resource that is empty
+  // (every load reads 0) for whole tiles, so all paths run the same in-place
+  // adds and the accumulators are not copied.
+  uint32_t part_bytes = 0;
+  const int sidx = split ? split - 1 : 0;
+  float* part_base = p.partial ? p.partial + (size_t)sidx * (lg2::BF * lg2::BT) : nullptr;
+  const uint32_t poff = (uint32_t)(wave * (NI * NJ * 1024) + 16 * lane);  // [wave][i][j][lane] f32x4
+  if (split) {
+    uint32_t* sync = p.split_sync + 2 * sidx;
+    if (tid == 0) *lds_word = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*lds_word == 0u) {
+      const brsrc_t r_out = make_rsrc(part_base, lg2::BF * lg2::BT * 4);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r_out,
+                                                 (int)(poff + (i * NJ + j) * 1024), 0, kAuxDevice);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are done
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    for (uint32_t it = 0; it < kSplitSpinLimit; ++it) {
+      if (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    part_bytes = lg2::BF * lg2::BT * 4;
+  }
+  {
+    const brsrc_t r_part = make_rsrc(part_base, part_bytes);
+    // one row of fragments in flight at a time; the empty asm pins each sum
+    // in its accumulator registers (otherwise the adds sink to the stores
+    // below and the loaded values are spilled)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[i][j] += __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_part, (int)(poff + (i * NJ + j) * 1024), 0, kAuxDevice));
+        asm volatile("" : "+v"(acc[i][j]));
+      }
+    }
+  }
+
   // ---- store (bf16) through LDS, so that global writes are whole rows ----
   // The K loop's last barrier has freed all tiles.  Each wave stages its
-  // 64-token x 128-feature tile as [64 rows][256 bytes] in 16 KB of its own
-  // (waves 2w', 2w' + 1 share one 32 KB tile array); 16-byte chunk c of row t
-  // sits at position c ^ (t % 16), so the 8-byte writes (16 rows x 4 lanes)
-  // and the 16-byte row reads are free of bank conflicts.
+  // WT x WF tile as [WT rows][2 WF bytes] in 16 KB of its own (waves 2w',
+  // 2w' + 1 share one 32 KB tile array).  The 16-byte chunk c of row t sits at
+  // position c ^ (t % 16) for 256-byte rows and c ^ ((t / 2) % 8) for 128-byte
+  // rows, so the 8-byte writes (16 rows x 4 lanes) and the 16-byte row reads
+  // are free of bank conflicts.
+  constexpr int CPR = WF / 8;  // 16-byte chunks per staged row
+  auto spos = [](int row, int c) { return CPR == 16 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7)); };
   uint8_t* stg = ((wave >> 1) == 0 ? lds.a[0] : (wave >> 1) == 1 ? lds.a[1] : (wave >> 1) == 2 ? lds.w[0] : lds.w[1]) +
                  16384 * (wave & 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int row = 16 * j + lr;
       const int col = 16 * i + 4 * lq;  // 4 features: chunk col / 8, half (col / 4) % 2
       const f32x4 v = acc[i][j];
-      *reinterpret_cast<u32x2*>(stg + row * 256 + ((((col >> 3) ^ (row & 15))) << 4) + ((col & 4) << 1)) =
+      *reinterpret_cast<u32x2*>(stg + row * (2 * WF) + (spos(row, col >> 3) << 4) + ((col & 4) << 1)) =
           u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are done
   __builtin_amdgcn_wave_barrier();
   const bool vec_ok = (p.N & 7) == 0;
-  const int c = lane & 15;
+  const int c = lane % CPR;
   const int64_t f = f0 + wf + 8 * c;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int row = 4 * k + (lane >> 4);
+  for (int k = 0; k < WT * CPR / 64; ++k) {
+    const int row = (64 / CPR) * k + lane / CPR;
     const int64_t t = t0 + wt + row;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * (2 * WF) + (spos(row, c) << 4));
     if (t >= p.M || f >= p.N) continue;
     uint16_t* dst = p.out + t * p.N + f;
     if (vec_ok && f + 8 <= p.N) {
@@ -406,26 +508,92 @@ __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, 
   __shared__ __align__(16) uint8_t sw1[T::W];
   __shared__ __align__(16) uint8_t sa0[lg2::ATILEB];
   __shared__ __align__(16) uint8_t sa1[lg2::ATILEB];
+  __shared__ uint32_t lds_word;
   const lg2::Lds lds{{sw0, sw1}, {sa0, sa1}};
   const int tid = threadIdx.x;
-  const int bid = xcd_remap_l(blockIdx.x, gridDim.x);
-  const int tile_f = bid % p.tiles_f;
-  const int tile_t = bid / p.tiles_f;
+  const int nk = (int)((p.K + lg2::BK - 1) / lg2::BK);
+  // work item -> tile and K range: full tiles first (XCD-aware order), then
+  // the K halves of the split tiles, which run in the last round
+  int tile, k0 = 0, ks = nk, split = 0;
+  bool lora = true;
+  if ((int)blockIdx.x < p.full_tiles) {
+    tile = xcd_remap_l(blockIdx.x, p.full_tiles);
+  } else {
+    const int w = (int)blockIdx.x - p.full_tiles;
+    const int half = w & 1;
+    tile = p.full_tiles + (w >> 1);
+    split = (w >> 1) + 1;
+    k0 = half ? nk / 2 : 0;
+    ks = half ? nk - nk / 2 : nk / 2;
+    lora = half != 0;
+  }
+  const int tile_f = tile % p.tiles_f;
+  const int tile_t = tile / p.tiles_f;
   const int64_t f0 = (int64_t)tile_f * lg2::BF;
   const int64_t t0 = (int64_t)tile_t * lg2::BT;
-  const int nk = (int)((p.K + lg2::BK - 1) / lg2::BK);
-  // wave-uniform split; both roles pass the same number of barriers
+  // wave-uniform role split; both roles pass the same number of barriers
   if (tid >= 64 * lg2::kMfmaWaves)
-    gemm_producer<kBwd>(p, tab, lds, tid - 64 * lg2::kMfmaWaves, f0, t0, nk);
+    gemm_producer<kBwd>(p, tab, lds, tid - 64 * lg2::kMfmaWaves, f0, t0, k0, ks, lora, split, &lds_word);
   else
-    gemm_consumer<kBwd>(p, lds, tid, f0, t0, nk);
+    gemm_consumer<kBwd>(p, lds, tid, f0, t0, k0, ks, lora, split, &lds_word);
 }
 
-static void launch_linear_gemm(bool bwd, const GemmArgs& a, const Nf4Table& tab, hipStream_t stream) {
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// Tiles whose last round would leave at least half of the CUs idle are split
+// in K: with T tiles on C CUs (one workgroup per CU), the last T mod C <= C/2
+// tiles become 2 (T mod C) half-length work items, so the last round fills
+// the chip for half the time instead of half the chip for the full time.
+int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT);
+  const int cus = device_cus();
+  const int64_t rem = tiles % cus;
+  const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
+  if (tiles < cus || rem == 0 || rem > cus / 2 || nk < 8) return 0;
+  return (int)rem;
+}
+
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t ns = (size_t)gemm_split_tiles(M, N, K);
+  if (!ns) return 0;
+  return ns * lg2::BF * lg2::BT * sizeof(float) + ((2 * ns * sizeof(uint32_t) + 255) / 256) * 256;
+}
+
+// split_ws: gemm_split_ws_bytes(M, N, K) bytes (16-byte aligned), or null to
+// run every tile whole.
+static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, const Nf4Table& tab,
+                               hipStream_t stream) {
   GemmArgs p = a;
   p.tiles_f = (int)((p.N + lg2::BF - 1) / lg2::BF);
   p.tiles_t = (int)((p.M + lg2::BT - 1) / lg2::BT);
-  const int grid = p.tiles_f * p.tiles_t;
+  const int tiles = p.tiles_f * p.tiles_t;
+  const int ns = split_ws ? gemm_split_tiles(p.M, p.N, p.K) : 0;
+  p.full_tiles = tiles - ns;
+  p.nsplit = ns;
+  p.partial = nullptr;
+  p.split_sync = nullptr;
+  if (ns) {
+    p.partial = static_cast<float*>(split_ws);
+    p.split_sync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(split_ws) +
+                                               (size_t)ns * lg2::BF * lg2::BT * sizeof(float));
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((2 * ns + 255) / 256), dim3(256), 0, stream, p.split_sync, 2 * ns);
+  }
+  const int grid = tiles + ns;
   if (bwd)
     hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
   else
@@ -434,22 +602,22 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, const Nf4Table& tab,
 
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
-                     float s, const Nf4Table& tab, hipStream_t stream) {
+                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream) {
   GemmArgs p{};
   p.act = x; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = B; p.lora_b = u; p.out = h;
   p.M = M; p.K = n; p.N = m; p.wn = n; p.wm = m; p.r = r; p.s = s;
-  launch_linear_gemm(false, p, tab, stream);
+  launch_linear_gemm(false, p, split_ws, tab, stream);
 }
 
 // g is M x m_pad (m_pad = m, or m rounded up to 64 with zero columns when
 // m % 8 != 0, so every 16-byte chunk of the tensor is whole).
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
-                       int64_t m_pad, int r, float s, const Nf4Table& tab, hipStream_t stream) {
+                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream) {
   GemmArgs p{};
   p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = A; p.lora_b = v; p.out = gx;
   p.M = M; p.K = m_pad; p.N = n; p.wn = n; p.wm = m; p.r = r; p.s = s;
-  launch_linear_gemm(true, p, tab, stream);
+  launch_linear_gemm(true, p, split_ws, tab, stream);
 }
 
 }  // namespace qlora

@@ -119,7 +119,12 @@ def test_bwd_argument_errors(lib):
 
 def test_workspace_sizes(lib):
     assert lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16) > 0
-    assert lib.qlora_workspace_bytes(1, 4096, 4096, 14336, 16) > lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16)
+    assert lib.qlora_workspace_bytes(1, 4096, 4096, 14336, 16) > 0
+    # 896 output tiles on 256 CUs: the last 128 tiles run as K halves whose fp32
+    # partial sums (256 x 256 each) live in the forward's workspace
+    assert lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16) >= 128 * 256 * 256 * 4
+    # 256 tiles fill the chip exactly: nothing is split
+    assert lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) < 16 << 20
     assert lib.qlora_workspace_bytes(0, 32, 100, 256, 8) == 0
     assert lib.qlora_workspace_bytes(7, 32, 256, 256, 8) == 0
     assert lib.qlora_workspace_bytes(0, 32, 256, 256, 0) == 0

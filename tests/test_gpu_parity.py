@@ -109,6 +109,34 @@ def test_ragged_shapes(Q, M, n, m, r, s):
     check_full(Q, inp["W"], inp, s, label=f"ragged M={M} n={n} m={m} r={r}")
 
 
+K_SPLIT = [
+    # (M, n, m, r, s): more 256 x 256 output tiles than CUs, with at most half
+    # a round left over: those last tiles run as two K halves whose fp32 sums
+    # meet in the workspace (ragged edges and two LoRA steps in the second)
+    (2304, 512, 8192, 16, 2.0),
+    (2400, 640, 7000, 40, 0.5),
+]
+
+
+@pytest.mark.parametrize("M,n,m,r,s", K_SPLIT)
+def test_k_split_last_round(Q, M, n, m, r, s):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // 256) * -(-m // 256)
+    rem = tiles % cus
+    if not (tiles > cus and 0 < rem <= cus // 2):
+        pytest.skip(f"{tiles} tiles on {cus} CUs: no K split")
+    lib = Q._lib.load()
+    assert lib.qlora_workspace_bytes(0, M, n, m, r) >= rem * 256 * 256 * 4, "split partials not in the workspace"
+    inp = QI.custom_inputs(seed=M + 3 * m + r, M=M, n=n, m=m, r=r)
+    got, _ = check_full(Q, inp["W"], inp, s, need_bwd=False, label=f"k-split M={M} n={n} m={m} r={r}")
+    say("k-split determinism")
+    x, A, B = dev_bf16(inp["x"]), dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    for _ in range(2):
+        h2, u2 = Q.linear_fwd(x, got["q"], A, B, s)
+        torch.cuda.synchronize()
+        assert torch.equal(h2, got["h"]) and torch.equal(u2, got["u"])
+
+
 SMALL_M = [
     # (M, n, m, r, s) on the weight-streaming path (M <= 32): K chunks of 2048,
     # 256-k pieces per wave, groups of 128 features
