@@ -40,9 +40,9 @@ BF16_PEAK_TFLOPS = 2500.0
 # GEMM source they were taken on: reported as null once it changes.
 GEMM_SRC = os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", "gemm_linear.hip")
 GEMM_TRAFFIC = {
-    "src_sha1": "3207302a681d3a39b98a675dfe6888406df027bf",
-    "fwd_gemm": {"fetch": 2 * 297272.06 * 1024, "write": 117635.64 * 1024},
-    "dgrad_gemm": {"fetch": 2 * 176958.81 * 1024, "write": 33824.61 * 1024},
+    "src_sha1": "e879cccf70df50ad0a2634948ebf8d12f0941c86",
+    "fwd_gemm": {"fetch": 2 * 299448.88 * 1024, "write": 147468.00 * 1024},
+    "dgrad_gemm": {"fetch": 2 * 176452.85 * 1024, "write": 32768.00 * 1024},
 }
 
 
