@@ -9,18 +9,21 @@
 //   - the (out-feature x K) plane of each layer is cut into work items of
 //     up to 16 blocks of 16 features x one K chunk of 2048, sized so that a
 //     launch has about two workgroups per CU;
-//   - a workgroup (4 waves) stages its x chunk (M x 2048 bf16, 64 or 128 KB)
-//     in LDS once, with line-coalesced loads, and each wave takes a quarter
-//     of the chunk (512 k) for all the item's feature blocks;
+//   - each of a workgroup's 4 waves takes a quarter of the chunk (512 k) for
+//     all the item's feature blocks and stages only its own quarter of x
+//     (M x 512 bf16) in LDS, with line-coalesced loads, so no wave waits for
+//     another before its main loop;
 //   - a wave streams the codes as MFMA A fragments: per 16-feature block and
 //     256-k piece every lane loads 32 contiguous bytes (8 code words, one
 //     64-weight block, so one magnitude table per 64 weights), dequantizes a
 //     word straight into the 8 bf16 of one 16x16x32 MFMA A operand, and reads
 //     the matching x fragment from LDS;
+//   - u = x A^T runs in extra workgroups of the same launch, one per layer
+//     and K chunk, next to the dequantizing ones (a launch fits in one round
+//     of the chip, so they add no tail);
 //   - the four waves' partial sums are reduced through LDS in a fixed order
-//     and written as fp32 partials per K chunk; the last feature group of a
-//     chunk also writes that chunk's u = x_chunk A_chunk^T; a second launch
-//     sums the chunks in order and adds s u B^T.
+//     and written as fp32 partials (h and u per K chunk); a second launch sums
+//     the chunks in order and adds s u B^T with MFMAs.
 // Within a 256-k piece, MFMA step q takes from lane group g (lanes 16g ..
 // 16g + 15) the k range 64g + 8q .. 64g + 8q + 7: the sum over k is the same,
 // only grouped differently, and both operands use the same grouping.
@@ -61,6 +64,7 @@ struct SmallLayer {
   int fbw;                  // 16-feature blocks per workgroup
   int ngroups;              // feature groups (fbw blocks each)
   int wg_begin;             // first workgroup of this layer in the launch
+  int u_begin;              // first u workgroup of this layer (after all dequantizing ones)
   int64_t out_begin;        // first finishing workgroup of this layer
 };
 
@@ -68,37 +72,125 @@ struct SmallArgs {
   SmallLayer L[sm::kMaxLayers];
   int count;
   int M;
+  int main_wgs;             // dequantizing workgroups; u workgroups follow
 };
 
-__device__ __forceinline__ int find_layer(const SmallArgs& a, int64_t key, bool by_out) {
+// which = 0: dequantizing workgroup, 1: finishing workgroup, 2: u workgroup
+__device__ __forceinline__ int find_layer(const SmallArgs& a, int64_t key, int which) {
   int li = 0;
 #pragma unroll
   for (int i = 1; i < sm::kMaxLayers; ++i)
-    if (i < a.count && (by_out ? a.L[i].out_begin : (int64_t)a.L[i].wg_begin) <= key) li = i;
+    if (i < a.count &&
+        (which == 1 ? a.L[i].out_begin : (int64_t)(which == 2 ? a.L[i].u_begin : a.L[i].wg_begin)) <= key)
+      li = i;
   return li;
 }
 
-// x chunk in LDS: token row t holds KC bf16; 16-byte chunk c of row t sits at
-// chunk position c ^ (t & 15), so the 16 tokens of one MFMA B fragment hit
-// 16 different bank groups.
+// A wave's x quarter in LDS: token row t holds 512 bf16 (64 chunks of 16 B);
+// chunk c of row t sits at position c ^ (t & 15), so the 16 tokens of one
+// MFMA B fragment hit 16 different bank groups.
 __device__ __forceinline__ uint32_t xsw(int t, int c) {
-  return (uint32_t)(t * (sm::KC * 2) + ((c ^ (t & 15)) << 4));
+  return (uint32_t)(t * (sm::KC / 4 * 2) + ((c ^ (t & 15)) << 4));
+}
+
+// u_chunk = x_chunk A_chunk^T for one layer and K chunk: each wave stages its
+// quarter of x and runs 16 MFMA steps per rank block of 16 (A fragments two
+// steps ahead); the four waves' sums are reduced through LDS in a fixed order.
+template <int TB>
+__device__ void small_u_chunk(const SmallArgs& a, uint8_t* lds, f32x4* ured) {
+  constexpr int MP = 16 * TB;
+  constexpr int QK = sm::KC / 4;
+  constexpr int XQB = MP * QK * 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+  const int li = find_layer(a, blockIdx.x, 2);
+  const SmallLayer& Ly = a.L[li];
+  const int kc = (int)blockIdx.x - Ly.u_begin;
+  const int M = a.M;
+  const int64_t K = Ly.n;
+  const int r = Ly.r;
+  const int64_t k0 = (int64_t)kc * sm::KC;
+  const int kq = wave * QK;
+  uint8_t* xq = lds + wave * XQB;
+  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+  const brsrc_t rx = make_rsrc(Ly.x, xbytes);
+#pragma unroll
+  for (int t = 0; t < MP; ++t) {
+    const int64_t k = k0 + kq + 8 * lane;
+    const bool ok = t < M && k < K;
+    *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
+  }
+  const uint32_t arbytes = (uint32_t)((int64_t)r * K * 2);
+  const brsrc_t ra = make_rsrc(Ly.A, arbytes);
+  float* up = Ly.upart + (int64_t)kc * M * r;
+  const int RBn = (r + 15) >> 4;
+  for (int rb = 0; rb < RBn; ++rb) {
+    constexpr int NJ = QK / 32;
+    const int q = 16 * rb + lr;
+    auto load_a = [&](int j) -> u32x4 {
+      const int64_t k = k0 + kq + 32 * j + 8 * g;
+      const bool ok = q < r && k < K;
+      return bload128(ra, ok ? (uint32_t)(((int64_t)q * K + k) * 2) : arbytes);
+    };
+    f32x4 ua[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) ua[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 an0 = load_a(0), an1 = load_a(1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const u32x4 af = an0;
+      an0 = an1;
+      if (j + 2 < NJ) an1 = load_a(j + 2);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const u32x4 bf = *reinterpret_cast<const u32x4*>(xq + xsw(16 * tb + lr, 4 * j + g));
+        ua[tb] = mfma16x16x32(af, bf, ua[tb]);
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) ured[(wave * TB + tb) * 64 + lane] = ua[tb];
+    __syncthreads();
+    if (tid < TB * 64) {
+      const int ln = tid & 63, tb = tid >> 6;
+      f32x4 v = ured[(0 * TB + tb) * 64 + ln];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += ured[(w * TB + tb) * 64 + ln];
+      // rows are adapter rows 16 rb + 4 (ln / 16) + e, column token 16 tb + ln % 16
+      const int t = 16 * tb + (ln & 15);
+      if (t < M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qq = 16 * rb + 4 * (ln >> 4) + e;
+          if (qq < r) up[(int64_t)t * r + qq] = v[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
 }
 
 template <int TB>
 __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table tab) {
   constexpr int MP = 16 * TB;                 // padded token count
-  constexpr int XB = MP * sm::KC * 2;         // 64 KB per token block
+  constexpr int QK = sm::KC / 4;              // k per wave quarter
+  constexpr int XQB = MP * QK * 2;            // one wave's x quarter: 16 KB per token block
   constexpr int FBMAX = SmallTile<TB>::FBMAX;
-  __shared__ __align__(16) uint8_t lds[XB];
+  __shared__ __align__(16) uint8_t lds[4 * XQB];
   __shared__ __align__(16) f32x4 ured[4 * TB * 64];   // per-wave u partials of one rank block
+  if ((int)blockIdx.x >= a.main_wgs) {
+    small_u_chunk<TB>(a, lds, ured);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15;
   const int g = lane >> 4;
 
-  const int li = find_layer(a, blockIdx.x, false);
+  const int li = find_layer(a, blockIdx.x, 0);
   const SmallLayer& Ly = a.L[li];
   const int local = blockIdx.x - Ly.wg_begin;
   const int kc = local % Ly.nkc;
@@ -107,24 +199,22 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
   const int64_t K = Ly.n;
   const int64_t m = Ly.m;
   const int64_t k0 = (int64_t)kc * sm::KC;
-  const int kq = wave * (sm::KC / 4);        // this wave's quarter within the chunk
+  const int kq = wave * QK;                   // this wave's quarter within the chunk
   const int64_t f_base = (int64_t)fg * Ly.fbw * 16;
   const int64_t nfb = (m + 15) / 16;
   const int nb = (int)((nfb - (int64_t)fg * Ly.fbw) < Ly.fbw ? (nfb - (int64_t)fg * Ly.fbw) : Ly.fbw);
+  uint8_t* xq = lds + wave * XQB;
 
-  // ---- stage x[0:MP][k0 : k0 + KC] (zeros past M or K) ----
+  // ---- this wave's x quarter: x[0:MP][k0 + kq : + QK] (zeros past M or K);
+  // load t covers token row t, 64 chunks = 1 KB contiguous ----
   const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
   const brsrc_t rx = make_rsrc(Ly.x, xbytes);
-  constexpr int XPT = MP * (sm::KC / 8) / 256;   // 16-byte chunks per thread
-  u32x4 xr[XPT];
+  u32x4 xr[MP];
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int id = i * 256 + tid;
-    const int t = id / (sm::KC / 8);
-    const int c = id % (sm::KC / 8);
-    const int64_t k = k0 + 8 * c;
+  for (int t = 0; t < MP; ++t) {
+    const int64_t k = k0 + kq + 8 * lane;
     const bool ok = t < M && k < K;
-    xr[i] = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
+    xr[t] = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
   }
 
   // ---- codes of this wave: lane's 64-weight block for (feature block b, piece p)
@@ -157,12 +247,10 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
 #pragma unroll
   for (int i = 0; i < sm::kDepth; ++i) load_codes(i / sm::kPW, i % sm::kPW, cq0[i], cq1[i], abq[i], csq[i]);
 
+  // x quarter to LDS: read back only by this wave (LDS keeps a wave's
+  // accesses in order), so no workgroup barrier
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int id = i * 256 + tid;
-    *reinterpret_cast<u32x4*>(lds + xsw(id / (sm::KC / 8), id % (sm::KC / 8))) = xr[i];
-  }
-  __syncthreads();
+  for (int t = 0; t < MP; ++t) *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = xr[t];
 
   // ---- main loop over (feature block, piece), codes kDepth iterations ahead ----
   f32x4 acc[FBMAX][TB];
@@ -181,7 +269,7 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
     // keep the prefetch where it is: the scheduler would otherwise sink these
     // loads next to their use kDepth iterations later
     __builtin_amdgcn_sched_barrier(0);
-    const int cbase = (kq + sm::PIECE * p + 64 * g) / 8;   // 16-byte chunk of k for step 0
+    const int cbase = (sm::PIECE * p + 64 * g) / 8;   // 16-byte chunk of k for step 0
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       uint32_t o[4];
@@ -189,62 +277,9 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
       const u32x4 af = u32x4{o[0], o[1], o[2], o[3]};
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        const u32x4 bf = *reinterpret_cast<const u32x4*>(lds + xsw(16 * tb + lr, cbase + q));
+        const u32x4 bf = *reinterpret_cast<const u32x4*>(xq + xsw(16 * tb + lr, cbase + q));
         acc[b][tb] = mfma16x16x32(af, bf, acc[b][tb]);
       }
-    }
-  }
-
-  // ---- the last feature group of each chunk (usually the one with fewest
-  // blocks) forms u_chunk = x_chunk A_chunk^T, each wave over its quarter,
-  // one rank block of 16 at a time ----
-  if (fg == Ly.ngroups - 1) {
-    const int r = Ly.r;
-    const int RBn = (r + 15) >> 4;
-    const uint32_t arbytes = (uint32_t)((int64_t)r * K * 2);
-    const brsrc_t ra = make_rsrc(Ly.A, arbytes);
-    float* up = Ly.upart + (int64_t)kc * M * r;
-    constexpr int NJ = (sm::KC / 4) / 32;   // 16 MFMA steps over the wave's quarter
-    for (int rb = 0; rb < RBn; ++rb) {
-      const int q = 16 * rb + lr;
-      u32x4 af[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t k = k0 + kq + 32 * j + 8 * g;
-        const bool ok = q < r && k < K;
-        af[j] = bload128(ra, ok ? (uint32_t)(((int64_t)q * K + k) * 2) : arbytes);
-      }
-      f32x4 ua[TB];
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) ua[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int kl = kq + 32 * j + 8 * g;   // k within the chunk
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          const u32x4 bf = *reinterpret_cast<const u32x4*>(lds + xsw(16 * tb + lr, kl / 8));
-          ua[tb] = mfma16x16x32(af[j], bf, ua[tb]);
-        }
-      }
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) ured[(wave * TB + tb) * 64 + lane] = ua[tb];
-      __syncthreads();
-      if (tid < TB * 64) {
-        const int ln = tid & 63, tb = tid >> 6;
-        f32x4 v = ured[(0 * TB + tb) * 64 + ln];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) v += ured[(w * TB + tb) * 64 + ln];
-        // rows are adapter rows 16 rb + 4 (ln / 16) + e, column token 16 tb + ln % 16
-        const int t = 16 * tb + (ln & 15);
-        if (t < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int qq = 16 * rb + 4 * (ln >> 4) + e;
-            if (qq < r) up[(int64_t)t * r + qq] = v[e];
-          }
-        }
-      }
-      __syncthreads();
     }
   }
 
@@ -269,113 +304,127 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
     const int t = 16 * tb + (ln & 15);
     const int64_t f = f_base + 16 * b + 4 * (ln >> 4);
     if (t < M) {
+      if ((m & 3) == 0 && f + 4 <= m) {
+        *reinterpret_cast<f32x4*>(hp + (int64_t)t * m + f) = v;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (f + e < m) hp[(int64_t)t * m + f + e] = v[e];
+        for (int e = 0; e < 4; ++e)
+          if (f + e < m) hp[(int64_t)t * m + f + e] = v[e];
+      }
     }
   }
 }
 
 // h[t][f] = bf16(sum_c hpart[c][t][f] + s * sum_q u[t][q] B[f][q]) with
-// u[t][q] = sum_c upart[c][t][q] (chunk order).  One workgroup finishes 128
-// features of one layer for every token: the B rows of those features and u
-// are staged in LDS; thread (token t, segment j) forms features
-// 8j .. 8j + 7 for tokens t and t + 16.  The layer's first workgroup also
-// writes u_out.
+// u[t][q] = sum over chunks (in chunk order) of upart.  One
+// workgroup (4 waves) finishes 64 features of one layer for every token, in
+// the MFMA C layout: wave w takes feature block w (16 features); lane (lr, g)
+// holds features 4 g .. 4 g + 3 of token 16 tb + lr, which is one 16-byte
+// vector of each chunk's partial.  s u B^T runs as MFMAs with the B rows as A
+// operand and s u^T, split into bf16 hi + lo, as B operand.  The layer's
+// first workgroup also writes u_out.
+template <int TB>
 __global__ __launch_bounds__(256) void small_reduce_kernel(SmallArgs a) {
   __shared__ float su[32 * kMaxRank];
-  __shared__ __align__(16) uint16_t sb[128 * kMaxRank];
-  const int li = find_layer(a, blockIdx.x, true);
+  const int li = find_layer(a, blockIdx.x, 1);
   const SmallLayer& Ly = a.L[li];
   const int tile = (int)(blockIdx.x - Ly.out_begin);
   const int M = a.M;
   const int64_t m = Ly.m;
   const int r = Ly.r;
   const int nkc = Ly.nkc;
+  const int nparts = nkc;
   const int tid = threadIdx.x;
-  const int64_t fbase = (int64_t)tile * 128;
-  const int nf_tile = (int)((m - fbase) < 128 ? (m - fbase) : 128);
-  // chunk partials are loaded 8 at a time before they are summed (in chunk
-  // order), so the loads of one thread overlap instead of forming a chain
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+  // u partials are loaded 8 at a time before they are summed (in order), so
+  // the loads of one thread overlap instead of forming a chain
   for (int idx = tid; idx < M * r; idx += 256) {
     float uq = 0.0f;
-    for (int c0 = 0; c0 < nkc; c0 += 8) {
+    for (int c0 = 0; c0 < nparts; c0 += 8) {
       float v[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = (c0 + c < nkc) ? Ly.upart[(int64_t)(c0 + c) * M * r + idx] : 0.0f;
+      for (int c = 0; c < 8; ++c) v[c] = (c0 + c < nparts) ? Ly.upart[(int64_t)(c0 + c) * M * r + idx] : 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        if (c0 + c < nkc) uq += v[c];
+        if (c0 + c < nparts) uq += v[c];
     }
     su[idx] = uq;
     if (Ly.u_out && tile == 0) Ly.u_out[idx] = uq;
   }
-  {
-    // B rows fbase .. fbase + nf_tile - 1 are one contiguous run of bf16
-    const uint16_t* src = Ly.B + fbase * r;
-    const int cnt = nf_tile * r;
-    if ((cnt & 7) == 0) {
-      for (int i = tid; i < cnt / 8; i += 256)
-        reinterpret_cast<u32x4*>(sb)[i] = reinterpret_cast<const u32x4*>(src)[i];
-    } else {
-      for (int i = tid; i < cnt; i += 256) sb[i] = src[i];
-    }
-  }
   __syncthreads();
-  const int j = tid & 15;
-  const int nf = nf_tile - 8 * j;   // features of this thread (<= 0: none)
-  if (nf <= 0) return;
-  const int64_t f0 = fbase + 8 * j;
-  const bool vec = (m & 7) == 0;
-  for (int t = tid >> 4; t < M; t += 16) {
-    float acc[8];
+  const int64_t fa = (int64_t)tile * 64 + 16 * wave + lr;   // B row of this lane's A fragment
+  const int64_t fc = (int64_t)tile * 64 + 16 * wave + 4 * g;  // this lane's 4 output features
+  const int QB = (r + 31) / 32;
+  const uint32_t bbytes = (uint32_t)(m * r * 2);
+  const brsrc_t rbm = make_rsrc(Ly.B, bbytes);
+  const uint32_t hbytes = (uint32_t)((int64_t)nkc * M * m * 4);
+  const brsrc_t rhp = make_rsrc(Ly.hpart, hbytes);
+  const bool v4 = (m & 3) == 0 && fc + 4 <= m;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    if (vec) {
-      for (int c0 = 0; c0 < nkc; c0 += 4) {
-        f32x4 v[4][2];
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t = 16 * tb + lr;
+    // chunk partials first (8 in flight), then the adapter term
+    f32x4 hs = {0.f, 0.f, 0.f, 0.f};
+    if (v4) {
+      for (int c0 = 0; c0 < nkc; c0 += 8) {
+        u32x4 w[8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4* hp = reinterpret_cast<const f32x4*>(Ly.hpart + ((int64_t)(c0 + c) * M + t) * m + f0);
-          v[c][0] = (c0 + c < nkc) ? hp[0] : f32x4{0.f, 0.f, 0.f, 0.f};
-          v[c][1] = (c0 + c < nkc) ? hp[1] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int c = 0; c < 8; ++c)
+          w[c] = bload128(rhp, (c0 + c < nkc && t < M) ? (uint32_t)((((int64_t)(c0 + c) * M + t) * m + fc) * 4) : hbytes);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c0 + c < nkc) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { acc[e] += v[c][0][e]; acc[4 + e] += v[c][1][e]; }
-          }
-        }
+        for (int c = 0; c < 8; ++c)
+          if (c0 + c < nkc) hs += __builtin_bit_cast(f32x4, w[c]);
       }
-    } else {
-      for (int c = 0; c < nkc; ++c) {
-        const float* hp = Ly.hpart + ((int64_t)c * M + t) * m + f0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e < nf) acc[e] += hp[e];
-      }
+    } else if (t < M) {
+      for (int c = 0; c < nkc; ++c)
+        for (int e = 0; e < 4; ++e)
+          if (fc + e < m) hs[e] += Ly.hpart[((int64_t)c * M + t) * m + fc + e];
     }
-    uint32_t outw[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      float lo0 = 0.0f, lo1 = 0.0f;
-      const uint16_t* b0 = sb + (8 * j + e) * r;
-      const uint16_t* b1 = b0 + r;
-      for (int q = 0; q < r; ++q) {
-        const float uq = su[t * r + q];
-        lo0 += uq * bf16_lo_to_f32((uint32_t)b0[q]);
-        lo1 += uq * bf16_lo_to_f32((uint32_t)b1[q]);
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) {
+      // A: B[fa][32 qb + 8 g .. + 7] (zeros past m or r)
+      uint32_t av[4] = {0u, 0u, 0u, 0u};
+      const int q0 = 32 * qb + 8 * g;
+      if (fa < m) {
+        if ((r & 7) == 0 && q0 + 8 <= r) {
+          const u32x4 w = bload128(rbm, (uint32_t)((fa * r + q0) * 2));
+          av[0] = w[0]; av[1] = w[1]; av[2] = w[2]; av[3] = w[3];
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (q0 + e < r) av[e >> 1] |= (uint32_t)Ly.B[fa * r + q0 + e] << (16 * (e & 1));
+        }
       }
-      outw[e / 2] = pack_bf16x2(acc[e] + Ly.s * lo0, acc[e + 1] + Ly.s * lo1);
-    }
-    uint16_t* dst = Ly.h + (int64_t)t * m + f0;
-    if (vec) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{outw[0], outw[1], outw[2], outw[3]};
-    } else {
+      // B operand: s u[t][32 qb + 8 g .. + 7] as bf16 hi + lo (zeros past M or r)
+      uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < nf) dst[e] = (uint16_t)((outw[e / 2] >> (16 * (e & 1))) & 0xFFFFu);
+      for (int e = 0; e < 4; ++e) {
+        float uv[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int q = q0 + 2 * e + h2;
+          uv[h2] = (t < M && q < r) ? Ly.s * su[t * r + q] : 0.0f;
+        }
+        float h0, l0, h1, l1;
+        split_bf16(uv[0], h0, l0);
+        split_bf16(uv[1], h1, l1);
+        hi[e] = pack_bf16x2(h0, h1);
+        lo[e] = pack_bf16x2(l0, l1);
+      }
+      const u32x4 aa = u32x4{av[0], av[1], av[2], av[3]};
+      acc2 = mfma16x16x32(aa, u32x4{hi[0], hi[1], hi[2], hi[3]}, acc2);
+      acc2 = mfma16x16x32(aa, u32x4{lo[0], lo[1], lo[2], lo[3]}, acc2);
+    }
+    if (t >= M || fc >= m) continue;
+    const f32x4 v = hs + acc2;
+    uint16_t* dst = Ly.h + (int64_t)t * m + fc;
+    if (v4) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (fc + e < m) dst[e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu);
     }
   }
 }
@@ -390,7 +439,7 @@ static inline int64_t cdiv_s(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t small_nkc(int64_t n) { return cdiv_s(n, sm::KC); }
 
-// fp32 partial workspace of one layer: [nkc][M][m] + [nkc][M][r]
+// fp32 partial workspace of one layer: h [nkc][M][m] and u [nkc][M][r]
 size_t small_ws_bytes(int64_t M, int64_t n, int64_t m, int r) {
   const int64_t nkc = small_nkc(n);
   const size_t hb = (size_t)nkc * M * m * sizeof(float);
@@ -410,12 +459,12 @@ void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4T
   a.count = count;
   a.M = M;
   const int fbmax = M <= 16 ? SmallTile<1>::FBMAX : SmallTile<2>::FBMAX;
-  // feature blocks per workgroup: the fewest that keep the launch within two
-  // workgroups per CU (a launch a few workgroups over that would run a second,
-  // almost empty round), the same width for every layer
+  // feature blocks per workgroup: the fewest that keep the launch (with its
+  // u workgroups) within two workgroups per CU (a launch a few workgroups over
+  // that would run a second, almost empty round), the same width for every layer
   auto wgs_for = [&](int fbw) {
     int64_t w = 0;
-    for (int i = 0; i < count; ++i) w += small_nkc(layers[i].n) * cdiv_s(cdiv_s(layers[i].m, 16), fbw);
+    for (int i = 0; i < count; ++i) w += small_nkc(layers[i].n) * (cdiv_s(cdiv_s(layers[i].m, 16), fbw) + 1);
     return w;
   };
   int fbw = 1;
@@ -436,13 +485,21 @@ void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4T
     L.wg_begin = wg;
     L.out_begin = outs;
     wg += L.nkc * L.ngroups;
-    outs += cdiv_s(h.m, 128);
+    outs += cdiv_s(h.m, 64);
+  }
+  a.main_wgs = wg;
+  for (int i = 0; i < count; ++i) {
+    a.L[i].u_begin = wg;
+    wg += a.L[i].nkc;
   }
   if (M <= 16)
     hipLaunchKernelGGL(small_fwd_kernel<1>, dim3((unsigned)wg), dim3(256), 0, stream, a, tab);
   else
     hipLaunchKernelGGL(small_fwd_kernel<2>, dim3((unsigned)wg), dim3(256), 0, stream, a, tab);
-  hipLaunchKernelGGL(small_reduce_kernel, dim3((unsigned)outs), dim3(256), 0, stream, a);
+  if (M <= 16)
+    hipLaunchKernelGGL(small_reduce_kernel<1>, dim3((unsigned)outs), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(small_reduce_kernel<2>, dim3((unsigned)outs), dim3(256), 0, stream, a);
 }
 
 }  // namespace qlora
