@@ -35,7 +35,7 @@ namespace sm {
 constexpr int KC = 2048;     // K per chunk
 constexpr int PIECE = 256;   // k per piece (32 bytes of codes per lane)
 constexpr int kPW = (KC / 4) / PIECE;   // pieces per wave and feature block (2)
-constexpr int kDepth = 6;    // code pieces in flight per wave
+constexpr int kDepth = 2;    // code pieces in flight per wave (deeper queues only delay x)
 constexpr int kMaxLayers = 8;
 constexpr int kTargetWGs = 512;         // two workgroups per CU
 }  // namespace sm
@@ -227,16 +227,18 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
   const brsrc_t rc2 = make_rsrc(Ly.c2, c2bytes);
   // No per-lane bounds checks: rows past m lie past the end of the packed
   // weight (the buffer range reads them as 0); k past K within a row reads the
-  // next row's codes, which meet the zero-padded x and add nothing.
+  // next row's codes, which meet the zero-padded x and add nothing.  Blocks
+  // past nb (prefetched, never used) get an offset past the end: the choice
+  // is the same for the whole wave, so it costs no vector instruction.
   const uint32_t row_step = (uint32_t)(16 * K / 2);   // bytes of codes per feature block
   const uint32_t cbase_off = (uint32_t)(((f_base + lr) * K + k0 + kq + 64 * g) / 2);
   auto load_codes = [&](int b, int p, u32x4& c0, u32x4& c1, uint32_t& ab, float& cs) {
-    const uint32_t off = b < nb ? cbase_off + (uint32_t)b * row_step + (uint32_t)p * (sm::PIECE / 2) : cbytes;
+    const uint32_t off = cbase_off + (b < nb ? (uint32_t)b * row_step + (uint32_t)p * (sm::PIECE / 2) : cbytes);
     c0 = bload128(rc, off);
     c1 = bload128(rc, off + 16);
     const uint32_t blk = off / (kBlock / 2);
-    ab = bload8(rab, b < nb ? blk : abytes);
-    cs = __uint_as_float(bload32(rc2, b < nb ? ((blk >> 8) << 2) : c2bytes));
+    ab = bload8(rab, blk);
+    cs = __uint_as_float(bload32(rc2, (blk >> 8) << 2));
   };
 
   // first pieces' codes in flight while x lands
@@ -248,9 +250,19 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
   for (int i = 0; i < sm::kDepth; ++i) load_codes(i / sm::kPW, i % sm::kPW, cq0[i], cq1[i], abq[i], csq[i]);
 
   // x quarter to LDS: read back only by this wave (LDS keeps a wave's
-  // accesses in order), so no workgroup barrier
+  // accesses in order), so no workgroup barrier.  Up to 16 tokens the wave
+  // then reads all its MFMA B fragments once and keeps them in registers (64
+  // VGPRs: fragment (p, q) of lane (lr, g) is x[lr][kq + 256 p + 64 g + 8 q ..
+  // + 7], the same for every feature block).
+  constexpr bool kXReg = TB == 1;
+  u32x4 xf[kXReg ? sm::kPW * 8 : 1];
 #pragma unroll
   for (int t = 0; t < MP; ++t) *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = xr[t];
+  if constexpr (kXReg) {
+#pragma unroll
+    for (int j = 0; j < sm::kPW * 8; ++j)
+      xf[j] = *reinterpret_cast<const u32x4*>(xq + xsw(lr, (sm::PIECE * (j >> 3) + 64 * g) / 8 + (j & 7)));
+  }
 
   // ---- main loop over (feature block, piece), codes kDepth iterations ahead ----
   f32x4 acc[FBMAX][TB];
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
       const u32x4 af = u32x4{o[0], o[1], o[2], o[3]};
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        const u32x4 bf = *reinterpret_cast<const u32x4*>(xq + xsw(16 * tb + lr, cbase + q));
+        const u32x4 bf = kXReg ? xf[8 * p + q] : *reinterpret_cast<const u32x4*>(xq + xsw(16 * tb + lr, cbase + q));
         acc[b][tb] = mfma16x16x32(af, bf, acc[b][tb]);
       }
     }
@@ -323,6 +335,149 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
 // vector of each chunk's partial.  s u B^T runs as MFMAs with the B rows as A
 // operand and s u^T, split into bf16 hi + lo, as B operand.  The layer's
 // first workgroup also writes u_out.
+//
+// With 16-byte rows (r a multiple of 8, m of 4) every lane loads what it
+// needs directly, all loads independent: its 16-byte vector of each chunk's
+// h partial, its B fragment, and the u partials of its 8 ranks, which it sums
+// in chunk order itself (every wave of a tile repeats this small sum).
+template <int TB>
+__device__ void small_reduce_aligned(const SmallLayer& Ly, int tile, int M) {
+  const int64_t m = Ly.m;
+  const int r = Ly.r;
+  const int nkc = Ly.nkc;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+  const int64_t fa = (int64_t)tile * 64 + 16 * wave + lr;   // B row of this lane's A fragment
+  const int64_t fc = (int64_t)tile * 64 + 16 * wave + 4 * g;  // this lane's 4 output features
+  const int QB = (r + 31) / 32;
+  constexpr int kQB = kMaxRank / 32;
+  constexpr int kC = 8;                                       // chunks per batch of loads
+  const uint32_t bbytes = (uint32_t)(m * r * 2);
+  const brsrc_t rbm = make_rsrc(Ly.B, bbytes);
+  const uint32_t hbytes = (uint32_t)((int64_t)nkc * M * m * 4);
+  const brsrc_t rhp = make_rsrc(Ly.hpart, hbytes);
+  const uint32_t ubytes = (uint32_t)((int64_t)nkc * M * r * 4);
+  const brsrc_t rup = make_rsrc(Ly.upart, ubytes);
+  // B fragment of rank block qb: B[fa][32 qb + 8 g .. + 7] (zeros past m or r)
+  auto load_b = [&](int qb) {
+    const int q0 = 32 * qb + 8 * g;
+    return bload128(rbm, (qb < QB && fa < m && q0 < r) ? (uint32_t)((fa * r + q0) * 2) : bbytes);
+  };
+  // B operand of one rank block: s u as bf16 hi + lo
+  auto su_split = [&](const f32x4& u0, const f32x4& u1, u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = Ly.s * (e < 2 ? u0[2 * e] : u1[2 * e - 4]);
+      const float v1 = Ly.s * (e < 2 ? u0[2 * e + 1] : u1[2 * e - 3]);
+      float h0, l0, h1, l1;
+      split_bf16(v0, h0, l0);
+      split_bf16(v1, h1, l1);
+      hi[e] = pack_bf16x2(h0, h1);
+      lo[e] = pack_bf16x2(l0, l1);
+    }
+  };
+  auto store_h = [&](int t, const f32x4& v) {
+    uint16_t* dst = Ly.h + (int64_t)t * m + fc;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  };
+  if (nkc <= kC && QB == 1) {
+    // the common shape in one round of loads: every load is issued (zeros
+    // past nkc, M or m) before the first sum
+    const int q0 = 8 * g;
+    const u32x4 b0 = load_b(0);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int t = 16 * tb + lr;
+      const bool tv = t < M;
+      u32x4 w[kC], w0[kC], w1[kC];
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        w[c] = bload128(rhp, (c < nkc && tv && fc < m) ? (uint32_t)((((int64_t)c * M + t) * m + fc) * 4) : hbytes);
+        const bool uv = c < nkc && tv && q0 < r;
+        const uint32_t off = uv ? (uint32_t)((((int64_t)c * M + t) * r + q0) * 4) : ubytes;
+        w0[c] = bload128(rup, off);
+        w1[c] = bload128(rup, uv ? off + 16 : ubytes);
+      }
+      f32x4 hs = {0.f, 0.f, 0.f, 0.f}, u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+        if (c < nkc) {
+          hs += __builtin_bit_cast(f32x4, w[c]);
+          u0 += __builtin_bit_cast(f32x4, w0[c]);
+          u1 += __builtin_bit_cast(f32x4, w1[c]);
+        }
+      if (Ly.u_out && tile == 0 && wave == 0 && tv && q0 < r) {
+        *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0) = u0;
+        *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0 + 4) = u1;
+      }
+      u32x4 hi, lo;
+      su_split(u0, u1, hi, lo);
+      f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+      acc2 = mfma16x16x32(b0, hi, acc2);
+      acc2 = mfma16x16x32(b0, lo, acc2);
+      if (tv && fc < m) store_h(t, hs + acc2);
+    }
+    return;
+  }
+  u32x4 bw[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) bw[qb] = load_b(qb);
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t = 16 * tb + lr;
+    const bool tv = t < M;
+    // chunk partials of h, kC at a time
+    f32x4 hs = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nkc; c0 += kC) {
+      u32x4 w[kC];
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+        w[c] = bload128(rhp, (c0 + c < nkc && tv && fc < m) ? (uint32_t)((((int64_t)(c0 + c) * M + t) * m + fc) * 4) : hbytes);
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+        if (c0 + c < nkc) hs += __builtin_bit_cast(f32x4, w[c]);
+    }
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q0 = 32 * qb + 8 * g;
+      const bool qv = tv && q0 < r;
+      // u[t][q0 .. q0 + 7], summed over the chunks in order from 0
+      f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nkc; c0 += kC) {
+        u32x4 w0[kC], w1[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+          const uint32_t off = (c0 + c < nkc && qv) ? (uint32_t)((((int64_t)(c0 + c) * M + t) * r + q0) * 4) : ubytes;
+          w0[c] = bload128(rup, off);
+          w1[c] = bload128(rup, off == ubytes ? ubytes : off + 16);
+        }
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+          if (c0 + c < nkc) {
+            u0 += __builtin_bit_cast(f32x4, w0[c]);
+            u1 += __builtin_bit_cast(f32x4, w1[c]);
+          }
+      }
+      if (Ly.u_out && tile == 0 && wave == 0 && qv) {
+        *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0) = u0;
+        *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0 + 4) = u1;
+      }
+      u32x4 hi, lo;
+      su_split(u0, u1, hi, lo);
+      u32x4 aa = bw[0];
+#pragma unroll
+      for (int j = 1; j < kQB; ++j)
+        if (qb == j) aa = bw[j];
+      acc2 = mfma16x16x32(aa, hi, acc2);
+      acc2 = mfma16x16x32(aa, lo, acc2);
+    }
+    if (tv && fc < m) store_h(t, hs + acc2);
+  }
+}
+
 template <int TB>
 __global__ __launch_bounds__(256) void small_reduce_kernel(SmallArgs a) {
   __shared__ float su[32 * kMaxRank];
@@ -332,6 +487,10 @@ __global__ __launch_bounds__(256) void small_reduce_kernel(SmallArgs a) {
   const int M = a.M;
   const int64_t m = Ly.m;
   const int r = Ly.r;
+  if ((r & 7) == 0 && (m & 3) == 0) {
+    small_reduce_aligned<TB>(Ly, tile, M);
+    return;
+  }
   const int nkc = Ly.nkc;
   const int nparts = nkc;
   const int tid = threadIdx.x;
