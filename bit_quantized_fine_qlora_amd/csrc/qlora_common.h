@@ -35,12 +35,12 @@ struct Nf4Table {
 };
 
 // E4M3FN (bias 7, 3 mantissa bits) to fp32.  Only non-negative finite codes
-// occur on this path; the value is exact in fp32.
+// occur on this path; the value is exact in fp32.  gfx950's fp8 convert reads
+// the OCP E4M3FN format; on codes 0x00 .. 0x7e (subnormals included) it gives
+// the same bits as the field-by-field decode (normal: 2^(e-7) (1 + m/8),
+// subnormal: m 2^-9), checked exhaustively on the device.
 __device__ __forceinline__ float e4m3_decode(uint32_t a) {
-  const uint32_t e = (a >> 3) & 15u, mnt = a & 7u;
-  const float normal = __uint_as_float(((e + 120u) << 23) | (mnt << 20));
-  const float sub = (float)mnt * 0.001953125f;  // m * 2^-9
-  return e ? normal : sub;
+  return __builtin_amdgcn_cvt_f32_fp8((int)a, 0);
 }
 
 // Round-to-nearest-even E4M3FN code of v in [0, 1] (no saturation needed).
