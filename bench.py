@@ -255,7 +255,7 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
 
     kern = {}
-    for name in ("quantize", "fwd_gemm", "dgrad_gemm", "down_proj", "token_grad", "transpose"):
+    for name in ("quantize", "fwd_gemm", "dgrad_gemm", "down_proj", "gpass", "token_grad", "transpose"):
         cnt, tot = Q.profile_query(name)
         if cnt:
             kern[name] = {"launches": cnt, "avg_us": tot * 1e3 / cnt}

@@ -45,6 +45,11 @@ void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
                           hipStream_t stream);
+bool gpass_supported(int R);
+int gpass_splits_f(int64_t J, int R);
+int gpass_splits_t(int64_t M);
+void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
+                  float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream);
 
 namespace {
 
@@ -200,8 +205,9 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t Bt, part_uv, u, v, gA, gB, gpad, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, total;
   int su, sv, sa, sb;
+  bool gpass;     // v and grad_B from one read of g
   int64_t m_pad;  // row length of g as the kernels read it
 };
 
@@ -217,13 +223,16 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   w.sv = down_proj_splits(M, w.m_pad, r);
   w.sa = token_grad_splits(M, n, r);
   w.sb = token_grad_splits(M, w.m_pad, r);
-  w.Bt = L.take((size_t)w.m_pad * r * 2);
-  const int suv = w.su > w.sv ? w.su : w.sv;
+  w.gpass = gpass_supported(r);
+  w.Bt = w.gpass ? 0 : L.take((size_t)w.m_pad * r * 2);
+  const int suv = w.gpass ? w.su : (w.su > w.sv ? w.su : w.sv);
   w.part_uv = L.take((size_t)suv * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
   w.v = L.take((size_t)M * r * sizeof(float));
   w.gA = L.take((size_t)w.sa * n * r * sizeof(float));
-  w.gB = L.take((size_t)w.sb * w.m_pad * r * sizeof(float));
+  w.gB = w.gpass ? 0 : L.take((size_t)w.sb * w.m_pad * r * sizeof(float));
+  w.vpart = w.gpass ? L.take((size_t)gpass_splits_f(w.m_pad, r) * M * r * sizeof(float)) : 0;
+  w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
   w.total = L.total;
   return w;
 }
@@ -420,23 +429,30 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
     launch_down_proj(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs);
     uu = at<float>(workspace, w.u);
   }
-  uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
   float* v = at<float>(workspace, w.v);
-  {
-    Timed tm("transpose", hs);
-    launch_transpose_bf16(B, m, r, mk, Bt, hs);
-  }
-  {
-    Timed tm("down_proj", hs);
-    launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs);
+  if (w.gpass) {
+    // v = g B and grad_B = s g^T u from one read of g
+    Timed tm("gpass", hs);
+    launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), v,
+                 grad_B, hs);
+  } else {
+    uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
+    {
+      Timed tm("transpose", hs);
+      launch_transpose_bf16(B, m, r, mk, Bt, hs);
+    }
+    {
+      Timed tm("down_proj", hs);
+      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs);
+    }
+    {
+      Timed tm("token_grad", hs);
+      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
+    }
   }
   {
     Timed tm("token_grad", hs);
     launch_token_grad(x, M, n, n, v, r, s, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs);
-  }
-  {
-    Timed tm("token_grad", hs);
-    launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
   }
   if (grad_x) {
     Timed tm("dgrad_gemm", hs);

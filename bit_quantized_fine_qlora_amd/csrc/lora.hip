@@ -134,14 +134,27 @@ __global__ __launch_bounds__(256) void down_proj_kernel(const uint16_t* __restri
   }
 }
 
+// sum_k part[k * stride + i] for k = 0 .. n - 1, added in k order from 0;
+// the loads go out 8 at a time so that they overlap
+__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int n, int64_t stride, int64_t i) {
+  float s = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = k0 + c < n ? part[(int64_t)(k0 + c) * stride + i] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (k0 + c < n) s += v[c];
+  }
+  return s;
+}
+
 // out[i] = sum_s part[s][i] in split order (fp32)
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t count,
                                                             float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
-  float s = 0.0f;
-  for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * count + i];
-  out[i] = s;
+  out[i] = sum_splits(part, nsplit, count, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,6 +334,234 @@ __global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// One read of g for both products that need it:
+//   vpart[fs][t][q]  = sum_{f in feature tile fs} g[t][f] * B[f][q]
+//   gbpart[ts][f][q] = sum_{t in token tile ts}  g[t][f] * u[t][q]
+// (v = sum_fs vpart, grad_B = s sum_ts gbpart).  A workgroup owns 256
+// tokens x 512 features of g and walks them as 16 sub-tiles of 64 x 128
+// (feature sub-tile outer).  Per sub-tile every wave adds 16 tokens' worth
+// of v (A = g rows, B operand = B read transposed from its natural [f][q]
+// tile) and 32 features' worth of grad_B (A = g columns read transposed, B
+// operand = u as bf16 hi + lo planes [q][t]) into accumulators that live
+// through the whole walk.  R a multiple of 8 and at most 16 RB.
+// ---------------------------------------------------------------------------
+namespace gp {
+constexpr int TT = 64;        // tokens per sub-tile
+constexpr int FT = 128;       // features per sub-tile
+constexpr int ST = 4;         // sub-tiles along tokens per workgroup
+constexpr int GB = TT * 256;  // g sub-tile bytes
+}  // namespace gp
+
+template <int RB, int SF>
+__global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__ G, int64_t M, int64_t J,
+                                                    const uint16_t* __restrict__ Bm, int64_t m,
+                                                    const float* __restrict__ U, int R, float* __restrict__ vpart,
+                                                    float* __restrict__ gbpart) {
+  constexpr int BP = 32 * RB;                // B tile row pitch: 16 RB ranks
+  constexpr int BTB = gp::FT * BP;           // B tile bytes
+  constexpr int PLANE = RB * 16 * 128;       // u plane: 16 RB rows of 64 tokens
+  constexpr int STAGE = gp::GB + BTB + 2 * PLANE;
+  __shared__ __align__(16) uint8_t lds[2 * STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;
+  const int lk = lane >> 4;
+  const int fs = blockIdx.x;                 // feature tile (v partial index)
+  const int ts = blockIdx.y;                 // token tile (grad_B partial index)
+  const int64_t f0 = (int64_t)fs * gp::FT * SF;
+  const int64_t t0 = (int64_t)ts * gp::TT * gp::ST;
+
+  // Rank slots q >= R of the B tiles and u planes are never loaded: clear them.
+  if (R < 16 * RB) {
+    for (int id = tid; id < 2 * gp::FT * (16 * RB - R) / 8; id += 256) {
+      const int st = id / (gp::FT * (16 * RB - R) / 8);
+      const int rest = id % (gp::FT * (16 * RB - R) / 8);
+      const int f = rest / ((16 * RB - R) / 8);
+      const int c = rest % ((16 * RB - R) / 8);
+      *reinterpret_cast<u32x4*>(lds + st * STAGE + gp::GB + f * BP + 2 * R + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int id = tid; id < 2 * 2 * (16 * RB - R) * 8; id += 256) {
+      const int chunk = id & 7;
+      const int rest = id >> 3;
+      const int q = R + rest % (16 * RB - R);
+      const int pl = rest / (16 * RB - R);  // stage * 2 + plane
+      *reinterpret_cast<u32x4*>(lds + (pl >> 1) * STAGE + gp::GB + BTB + (pl & 1) * PLANE + swy(q, chunk)) =
+          u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const uint32_t gbytes = (uint32_t)(M * J * 2);
+  const uint32_t bbytes = (uint32_t)(m * R * 2);
+  const uint32_t ubytes = (uint32_t)(M * R * 4);
+  const brsrc_t rg = make_rsrc(G, gbytes);
+  const brsrc_t rb = make_rsrc(Bm, bbytes);
+  const brsrc_t ru = make_rsrc(U, ubytes);
+  const int prow = tid >> 4;
+  const int pc = tid & 15;
+  // 16-byte pieces of one B sub-tile (128 rows of R bf16), which is also the
+  // count of one u sub-tile (64 rows of R fp32)
+  const int npieces = gp::FT * R / 8;
+  constexpr int PPT = RB;                    // pieces per thread, upper bound (R <= 16 RB)
+
+  // sub-tile i: feature sub-tile i / ST, token sub-tile i % ST
+  auto load = [&](int i, u32x4(&gr)[4], u32x4(&br)[PPT], u32x4(&ur)[PPT]) {
+    const int64_t fb = f0 + (int64_t)(i / gp::ST) * gp::FT;
+    const int64_t tb = t0 + (int64_t)(i % gp::ST) * gp::TT;
+    const bool fok = fb + 8 * pc < J;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = tb + 16 * k + prow;
+      gr[k] = bload128(rg, (fok && t < M) ? (uint32_t)((t * J + fb + 8 * pc) * 2) : gbytes);
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = 256 * k + tid;
+      // B rows fb .. fb + 127 and u rows tb .. tb + 63 are contiguous ranges
+      br[k] = bload128(rb, (p < npieces && fb * R * 2 + 16 * p < (int64_t)bbytes) ? (uint32_t)(fb * R * 2 + 16 * p)
+                                                                                 : bbytes);
+      ur[k] = bload128(ru, (p < npieces && tb * R * 4 + 16 * p < (int64_t)ubytes)
+                               ? (uint32_t)(tb * R * 4 + 16 * p) : ubytes);
+    }
+  };
+  auto store = [&](int buf, const u32x4(&gr)[4], const u32x4(&br)[PPT], const u32x4(&ur)[PPT]) {
+    uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(base + swtg(16 * k + prow, pc)) = gr[k];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = 256 * k + tid;
+      if (p < npieces) {
+        const int f = (16 * p) / (2 * R);
+        const int cb = (16 * p) % (2 * R);
+        *reinterpret_cast<u32x4*>(base + gp::GB + f * BP + cb) = br[k];
+      }
+      if (p < npieces) {
+        // 4 fp32 of u: token t, ranks q .. q + 3 (R % 4 == 0)
+        const int t = (4 * p) / R;
+        const int q = (4 * p) % R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float h, l;
+          split_bf16(__uint_as_float(ur[k][e]), h, l);
+          const uint32_t off = swy(q + e, t >> 3) + (t & 7) * 2;
+          *reinterpret_cast<uint16_t*>(base + gp::GB + BTB + off) = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+          *reinterpret_cast<uint16_t*>(base + gp::GB + BTB + PLANE + off) = (uint16_t)(pack_bf16x2(l, 0.f) & 0xFFFFu);
+        }
+      }
+    }
+  };
+
+  f32x4 av[gp::ST][RB];        // v: tokens 64 ts' + 16 wave + 4 lk + e, rank 16 cb + lr
+  f32x4 ab[SF][2][RB];     // grad_B: features 128 fs' + 32 wave + 16 ib + 4 lk + e, rank 16 cb + lr
+#pragma unroll
+  for (int i = 0; i < gp::ST; ++i)
+#pragma unroll
+    for (int c = 0; c < RB; ++c) av[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < SF; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < RB; ++c) ab[i][j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tr_row = lr >> 2;
+  const int tr_c = lr & 3;
+  auto compute = [&](int buf, int i) {
+    const uint8_t* base = lds + buf * STAGE;
+    const int fsub = i / gp::ST, tsub = i % gp::ST;
+    // v += g[16 wave + lr][f] B[f][q] over the 128 features
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(base + swtg(16 * wave + lr, 4 * s4 + lk));
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        // B operand: rows f = 32 s4 + 8 lk + 4 h + lr / 4, ranks 16 cb + 4 (lr % 4) .. + 3
+        const uint8_t* p0 = base + gp::GB + (32 * s4 + 8 * lk + tr_row) * BP + 2 * (16 * cb + 4 * tr_c);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * BP));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        av[tsub][cb] = mfma16x16x32(a, u32x4{l2[0], l2[1], h2[0], h2[1]}, av[tsub][cb]);
+      }
+    }
+    // grad_B += g[t][32 wave + 16 ib + lr] u[t][q] over the 64 tokens
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 a[2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int t = 32 * kk + 8 * lk + tr_row;
+        const int c = 2 * (2 * wave + ib) + (tr_c >> 1);
+        const uint8_t* p0 = base + swtg(t, c) + (tr_c & 1) * 8;
+        const uint8_t* p1 = base + swtg(t + 4, c) + (tr_c & 1) * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        a[ib] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+      }
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        const uint32_t off = swy(16 * cb + lr, 4 * kk + lk);
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(base + gp::GB + BTB + off);
+        const u32x4 bl = *reinterpret_cast<const u32x4*>(base + gp::GB + BTB + PLANE + off);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          ab[fsub][ib][cb] = mfma16x16x32(a[ib], bh, ab[fsub][ib][cb]);
+          ab[fsub][ib][cb] = mfma16x16x32(a[ib], bl, ab[fsub][ib][cb]);
+        }
+      }
+    }
+  };
+
+  // D sub-tiles of loads in flight (register sets used round-robin), two LDS
+  // buffers: sub-tile i is stored into buffer i % 2 once every wave has left
+  // the compute of sub-tile i - 2 (the barrier of sub-tile i - 1)
+  constexpr int NS = gp::ST * SF;
+  constexpr int D = RB == 1 ? 4 : 2;
+  u32x4 gr[D][4], br[D][PPT], ur[D][PPT];
+#pragma unroll
+  for (int i = 0; i < D; ++i) load(i, gr[i], br[i], ur[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    store(i & 1, gr[i % D], br[i % D], ur[i % D]);
+    if (i + D < NS) load(i + D, gr[i % D], br[i % D], ur[i % D]);
+    __syncthreads();
+    compute(i & 1, i);
+  }
+
+  float* vdst = vpart + (int64_t)fs * M * R;
+#pragma unroll
+  for (int i = 0; i < gp::ST; ++i)
+#pragma unroll
+    for (int cb = 0; cb < RB; ++cb) {
+      const int q = 16 * cb + lr;
+      if (q >= R) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = t0 + gp::TT * i + 16 * wave + 4 * lk + e;
+        if (t < M) vdst[t * R + q] = av[i][cb][e];
+      }
+    }
+  float* bdst = gbpart + (int64_t)ts * J * R;
+#pragma unroll
+  for (int i = 0; i < SF; ++i)
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        const int q = 16 * cb + lr;
+        if (q >= R) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t f = f0 + gp::FT * i + 32 * wave + 16 * ib + 4 * lk + e;
+          if (f < J) bdst[f * R + q] = ab[i][ib][cb][e];
+        }
+      }
+}
+
 // out = bf16(s * sum_s part[s]) over the first Jout rows of part ([J][R] per
 // split); out is [Jout][R] or, when transpose_out, [R][Jout].
 __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restrict__ part, int nsplit, int64_t J,
@@ -328,9 +569,7 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restric
                                                           uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= Jout * R) return;
-  const int64_t stride = J * R;
-  float acc = 0.0f;
-  for (int k = 0; k < nsplit; ++k) acc += part[(int64_t)k * stride + i];
+  const float acc = sum_splits(part, nsplit, J * R, i);
   const uint16_t b = (uint16_t)(pack_bf16x2(s * acc, 0.f) & 0xFFFFu);
   if (!transpose_out) {
     out[i] = b;
@@ -416,6 +655,29 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
   const int64_t count = Jout * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
                      Jout, R, s, transpose_out, out);
+}
+
+// v and grad_B from one read of g (R % 8 == 0, R <= 32): vpart holds
+// gpass_splits_f(J, R) x M x R floats, gbpart gpass_splits_t(M) x J x R.
+bool gpass_supported(int R) { return R % 8 == 0 && R <= 32; }
+static inline int gpass_sf(int R) { return R <= 16 ? 4 : 2; }
+int gpass_splits_f(int64_t J, int R) { return (int)cdiv(J, gp::FT * gpass_sf(R)); }
+int gpass_splits_t(int64_t M) { return (int)cdiv(M, gp::TT * gp::ST); }
+
+void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
+                  float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream) {
+  const int sf = gpass_splits_f(J, R), st = gpass_splits_t(M);
+  const dim3 grid((unsigned)sf, (unsigned)st);
+  if (R <= 16)
+    hipLaunchKernelGGL((gpass_kernel<1, 4>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
+  else
+    hipLaunchKernelGGL((gpass_kernel<2, 2>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
+  const int64_t count = M * R;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
+                     v);
+  const int64_t gcount = m * R;
+  hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(gcount, 256)), dim3(256), 0, stream, gbpart, st, J, m,
+                     R, s, 0, grad_B);
 }
 
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,

@@ -100,6 +100,8 @@ RAGGED = [
     (513, 256, 520, 24, 0.75),
     (64, 128, 72, 64, 0.25),
     (257, 448, 259, 7, 3.0),
+    (200, 256, 1000, 32, 1.0),
+    (77, 128, 333, 8, 2.0),
 ]
 
 
