@@ -14,8 +14,12 @@ events on the stream the library launches on:
   - the forward alone and the backward alone of the same layer;
   - the small-token regime: the forward of all seven layers of the
     8B-shaped block at 16 tokens in one grouped call, and the quantization of
-    the block's seven weights, both against the HBM peak (the caches are
-    flushed by writing 1 GiB before every repetition).
+    the block's seven weights, both against the HBM peak;
+  - the adapter merge W_merged = bf16(W' + s B A) of the gate projection,
+    against the HBM peak.
+For the HBM-bound measurements the caches are flushed before every
+repetition by reading 1 GiB (a read evicts the working set cleanly; a write
+flush would leave dirty lines whose write-back lands in the timed kernel).
 """
 
 from __future__ import annotations
@@ -90,7 +94,7 @@ def timed_us(fn, reps, flush=None):
     ts = []
     for _ in range(reps):
         if flush is not None:
-            flush.fill_(1)
+            flush.sum()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -138,8 +142,27 @@ def small_token_block(Q, dev, reps):
                      "us": round(qmed, 2), "bytes": qbytes,
                      "GB/s": round(qbytes / (qmed * 1e-6) / 1e9, 1),
                      "hbm_frac": round(qbytes / (qmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "cache_flush": "1 GiB written before every repetition",
+        "cache_flush": "1 GiB read before every repetition",
     }
+
+
+def merge_bytes(m, n, r):
+    """Packed weight read, adapter read, merged bf16 weight written."""
+    numel = m * n
+    return numel // 2 + numel // 64 + 4 * ((numel // 64 + 255) // 256) + 2 * (r * n + m * r) + 2 * numel
+
+
+def adapter_merge(Q, q, A, B, s, reps):
+    """W_merged = bf16(W' + s B A) of one layer, cold caches."""
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.codes.device)
+    med, mn = timed_us(lambda: Q.merge_adapter(q, A, B, s), reps, flush)
+    r = A.shape[0]
+    mb = merge_bytes(q.m, q.n, r)
+    return {"workload": f"gate projection {q.m}x{q.n}, r={r}", "us": round(med, 2), "us_min": round(mn, 2),
+            "bytes": mb, "GB/s": round(mb / (med * 1e-6) / 1e9, 1),
+            "hbm_frac": round(mb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "cache_flush": "1 GiB read before every repetition"}
 
 
 def cpu_baseline(cfg, layer, tokens):
@@ -306,6 +329,7 @@ def main():
     }
     out.update(extra)
     if not args.no_extra:
+        out["adapter_merge"] = adapter_merge(Q, q, A, B, s, 10)
         del W, x, g, A, B, h, gx, ws_f, ws_b
         torch.cuda.empty_cache()
         out["small_tokens"] = small_token_block(Q, dev, 10)

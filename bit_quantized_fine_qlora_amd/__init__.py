@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     linear_bwd,
     linear_fwd,
     linear_fwd_grouped,
+    merge_adapter,
     nf4_table,
     profile_enable,
     profile_query,

@@ -90,6 +90,18 @@ def dequant_nf4_dq(q: QuantizedWeight) -> torch.Tensor:
     return out
 
 
+def merge_adapter(q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float) -> torch.Tensor:
+    """bf16(W' + s B A): the adapter folded into the dequantized weight (m x n bf16)."""
+    r = A.shape[0]
+    _need(A, torch.bfloat16, (r, q.n), "A")
+    _need(B, torch.bfloat16, (q.m, r), "B")
+    out = torch.empty((q.m, q.n), dtype=torch.bfloat16, device=q.codes.device)
+    st = _lib.load().qlora_merge_adapter(_ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2), q.m, q.n, r, float(s),
+                                         _ptr(A), _ptr(B), _ptr(out), _stream(q.codes.device))
+    _lib.check(st, "qlora_merge_adapter")
+    return out
+
+
 def _workspace(op, M, n, m, r, device, workspace):
     need = workspace_bytes(op, M, n, m, r)
     if workspace is None or workspace.numel() < need:

@@ -45,6 +45,9 @@ void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
                           hipStream_t stream);
+void launch_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m, int64_t n, int r,
+                          float s, const uint16_t* A, const uint16_t* B, uint16_t* out, const Nf4Table& tab,
+                          hipStream_t stream);
 bool gpass_supported(int R);
 int gpass_splits_f(int64_t J, int R);
 int gpass_splits_t(int64_t M);
@@ -295,6 +298,26 @@ qlora_status qlora_dequant_nf4_dq(const uint8_t* codes, const uint8_t* absmax8, 
   {
     Timed tm("dequant", s);
     launch_dequant(codes, absmax8, c2, m * n, W_out, table(), s);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m,
+                                 int64_t n, int32_t r, float s, const qlora_bf16* A, const qlora_bf16* B,
+                                 qlora_bf16* W_out, qlora_stream_t stream) {
+  if (!codes || !absmax8 || !c2 || !A || !B || !W_out) return QLORA_ERR_NULL;
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (r < 1 || r > kMaxRank) return QLORA_ERR_RANK;
+  if (!std::isfinite(s)) return QLORA_ERR_VALUE;
+  if ((int64_t)r * n * 2 >= ((int64_t)1 << 32)) return QLORA_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(A) || !aligned16(B) ||
+      !aligned16(W_out))
+    return QLORA_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("merge", hs);
+    launch_merge_adapter(codes, absmax8, c2, m, n, r, s, A, B, W_out, table(), hs);
   }
   return hip_status();
 }

@@ -102,6 +102,26 @@ qlora_status qlora_quantize_nf4_dq(const float* W, int64_t m, int64_t n, uint8_t
 qlora_status qlora_dequant_nf4_dq(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m,
                                   int64_t n, qlora_bf16* W_out, qlora_stream_t stream);
 
+/*
+ * Merge a trained adapter into the weight ("QLoRA: Efficient Fine-Tuning",
+ * Real-World Impact: W_merged = W0 + B A, no adapter cost at inference;
+ * "QLoRA & 4-bit Fine-Tuning", Followups to expect: dequantize to BF16, add
+ * the adapter, keep a 16-bit model), with the adapter's alpha/r scale:
+ *   W_out = bf16(W' + s B A),  W' = the bf16 dequantized weight above.
+ *   codes, absmax8, c2: the quantized m x n weight.
+ *   A        device, r x n bf16.      B  device, m x r bf16.
+ *   W_out    device out, m*n bf16.
+ * The product B A accumulates in fp32 and is added to W' with one fused
+ * multiply-add before the single rounding to bf16, so each element is the
+ * exactly rounded sum or one of its bf16 neighbours (the fp32 error is far
+ * below half a bf16 unit); with B = 0 or s = 0 it is W' bit for bit.
+ * Requires m >= 1, n >= 64, n % 64 == 0, r in 1..128, finite s,
+ * r * n < 2^31.  Every pointer 16-byte aligned.
+ */
+qlora_status qlora_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m,
+                                 int64_t n, int32_t r, float s, const qlora_bf16* A, const qlora_bf16* B,
+                                 qlora_bf16* W_out, qlora_stream_t stream);
+
 /* Operation ids for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1

@@ -29,6 +29,8 @@ What is computed, step by step (numpy; float64 unless a step fixes fp32):
                            code snippet's LoraConfig comment
   backward                 [P1] Step 4, Eq. 5 (adapter gradients), and the
                            chain rule of the forward for grad_x
+  adapter merge            [P1] Real-World Impact; [P4] Followups to expect
+                           (W' + s B A rounded once to bf16)
 
 Readings taken where the pages are silent or garbled (each is listed, with
 its reason, in the design notes of the repository):
@@ -173,6 +175,23 @@ def bf16_bits_rne(x) -> np.ndarray:
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even)
     out = np.where(take_hi, hi_bits, lo_bits) >> 16
     return out.astype(np.uint16)
+
+
+def bf16_bits_rne_f64(x) -> np.ndarray:
+    """bf16 bit patterns of float64 values, rounded once to nearest, ties even.
+
+    bf16 keeps 8 significant bits: with x = f 2^e (0.5 <= |f| < 1), the
+    result is rint(f 2^8) 2^(e - 8) (numpy's rint rounds ties to even), with
+    the exponent held at bf16's subnormal quantum 2^-133 for tiny values.
+    The rounded value is exact in fp32, whose top 16 bits are the pattern.
+    Finite inputs only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    r = np.rint(np.ldexp(x, 8 - e))
+    y = np.ldexp(r, e - 8)
+    return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def bf16_bits_to_float64(b) -> np.ndarray:
@@ -353,6 +372,22 @@ def linear_bwd(x, g, Wd, A, B, s: float, u=None):
     grad_A = s * (v.T @ x)
     grad_B = s * (g.T @ u)
     return dict(grad_x=grad_x, grad_A=grad_A, grad_B=grad_B, v=v)
+
+
+def merge_adapter(Wd_bits, A_bits, B_bits, s: float, m: int, n: int) -> np.ndarray:
+    """bf16 bit patterns of W' + s B A, summed exactly and rounded once.
+
+    [P1] Real-World Impact: after training, the adapter is merged into the
+    base weight, W_merged = W0 + B A, so inference runs a plain layer.
+    [P4] Followups to expect: the 4-bit weight is dequantized to BF16 first,
+    the adapter added, and a 16-bit weight kept.  The adapter term carries
+    s = alpha / r as in the forward.  Wd_bits: m*n bf16 patterns of W'
+    (dequant_nf4_dq), A_bits: r x n, B_bits: m x r bf16 patterns.
+    """
+    Wd = bf16_bits_to_float64(np.asarray(Wd_bits)).reshape(m, n)
+    A = bf16_bits_to_float64(np.asarray(A_bits))
+    B = bf16_bits_to_float64(np.asarray(B_bits))
+    return bf16_bits_rne_f64(Wd + s * (B @ A)).reshape(m, n)
 
 
 def linear_fwd_loops(x, Wd, A, B, s: float):

@@ -307,6 +307,69 @@ def test_quantizer_threshold_boundaries(Q):
     check_quantizer(q, O.quantize_nf4_dq(W))
 
 
+# ------------------------------------------------------------------ adapter merge
+
+def bf16_order(bits):
+    b = np.asarray(bits).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def check_merge(got_bits, want_bits, what):
+    # the kernel's fp32 sum differs from the exact one by far less than half a
+    # bf16 unit, so its rounding is the exact one or a neighbour
+    d = np.abs(bf16_order(got_bits) - bf16_order(want_bits))
+    assert d.max() <= 1, f"{what}: {int(d.max())} bf16 units off"
+    assert np.mean(d == 0) >= 0.99, f"{what}: only {np.mean(d == 0):.4f} exact"
+
+
+MERGE = [
+    # (m, n, r, s)
+    (256, 256, 8, 2.0),
+    (333, 192, 5, 0.5),
+    (64, 640, 128, 0.25),
+    (1, 64, 1, 1.0),
+    (100, 128, 32, 3.0),
+]
+
+
+@pytest.mark.parametrize("m,n,r,s", MERGE)
+def test_merge_adapter(Q, m, n, r, s):
+    inp = QI.custom_inputs(seed=7 * m + n + r, M=1, n=n, m=m, r=r)
+    qw = O.quantize_nf4_dq(inp["W"])   # oracle codes, uploaded as the kernel's input
+    q = Q.QuantizedWeight(codes=torch.from_numpy(qw["codes"]).cuda(), absmax8=torch.from_numpy(qw["absmax8"]).cuda(),
+                          c2=torch.from_numpy(qw["c2"]).cuda(), m=m, n=n)
+    Wd_bits = O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], m * n)
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    say(f"merge m={m} n={n} r={r}")
+    got = host_bits(Q.merge_adapter(q, A, B, s)).reshape(m, n)
+    check_merge(got, O.merge_adapter(Wd_bits, inp["A"], inp["B"], s, m, n), f"merge {m}x{n} r={r}")
+    # a zero adapter (B = 0, or s = 0) leaves the dequantized weight bit for bit
+    got0 = host_bits(Q.merge_adapter(q, A, torch.zeros_like(B), s)).reshape(-1)
+    assert np.array_equal(got0, Wd_bits), "merge with B = 0 differs from W'"
+    got1 = host_bits(Q.merge_adapter(q, A, B, 0.0)).reshape(-1)
+    assert np.array_equal(got1, Wd_bits), "merge with s = 0 differs from W'"
+
+
+def test_merge_adapter_full_size_gate(Q):
+    # the gate projection of the 8B-shaped block (14336 x 4096, r = 16), rows sampled
+    L = QI.CONFIGS[2]["layers"][0]
+    inp = QI.layer_inputs(2, L, tensors=("W", "A", "B"))
+    say(f"merge full size {L.m}x{L.n}: oracle quantize")
+    qw = O.quantize_nf4_dq(inp["W"])
+    q = Q.QuantizedWeight(codes=torch.from_numpy(qw["codes"]).cuda(), absmax8=torch.from_numpy(qw["absmax8"]).cuda(),
+                          c2=torch.from_numpy(qw["c2"]).cuda(), m=L.m, n=L.n)
+    A, B = dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    say("merge full size: gpu")
+    Wm = Q.merge_adapter(q, A, B, L.s)
+    rows = sample_indices(L.m, 128, 4242)
+    got = host_bits(Wm[torch.from_numpy(rows).cuda()])
+    Wr_bits = O.bf16_bits_rne_f64(O.dequant_rows(qw, L.m, L.n, rows)).reshape(-1)
+    want = O.merge_adapter(Wr_bits, inp["A"], inp["B"][rows], L.s, len(rows), L.n)
+    check_merge(got, want, "merge full-size gate (sampled rows)")
+    del Wm, q
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ full size
 
 def oracle_rows_for(W, rows):
