@@ -41,22 +41,26 @@ BF16_PEAK_TFLOPS = 2500.0
 # --pmc FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch),
 # scaled by what the same counters read for a plain 1 GiB device copy
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/).  Valid only for the
-# GEMM source they were taken on: reported as null once it changes.
-GEMM_SRC = os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", "gemm_linear.hip")
+# GEMM sources they were taken on (the kernel and the header it includes):
+# reported as null once either changes.
+GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "e879cccf70df50ad0a2634948ebf8d12f0941c86",
-    "fwd_gemm": {"fetch": 2 * 299448.88 * 1024, "write": 147468.00 * 1024},
-    "dgrad_gemm": {"fetch": 2 * 176452.85 * 1024, "write": 32768.00 * 1024},
+    "src_sha1": "458a76899d65a156bb08fde8cf16b4d0316ca6e4",
+    "fwd_gemm": {"fetch": 2 * 299440.7 * 1024, "write": 147468.0 * 1024},
+    "dgrad_gemm": {"fetch": 2 * 176414.6 * 1024, "write": 32768.0 * 1024},
 }
 
 
 def gemm_traffic(kernel):
     import hashlib
+    h = hashlib.sha1()
     try:
-        with open(GEMM_SRC, "rb") as f:
-            digest = hashlib.sha1(f.read()).hexdigest()
+        for path in GEMM_SRC:
+            with open(path, "rb") as f:
+                h.update(f.read())
     except OSError:
         return None
+    digest = h.hexdigest()
     if digest != GEMM_TRAFFIC["src_sha1"] or kernel not in GEMM_TRAFFIC:
         return None
     t = GEMM_TRAFFIC[kernel]

@@ -31,6 +31,25 @@ constexpr int CT = 128;   // columns per workgroup
 
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 
+// Workgroup id -> (column tile, row tile).  A 128-column tile uses half of
+// every 128-byte line of codes; the two tiles of a 256-column pair are given
+// ids 8 apart, so they run on the same XCD (ids go round-robin over the 8
+// XCDs) close in time and the second finds the line in that XCD's L2.  Needs
+// an even number of column tiles and a pair count that is a multiple of 8;
+// otherwise ids map in plain order.
+__device__ __forceinline__ void merge_tile(int L, int gx, int gy, int& bx, int& by) {
+  const int npairs = gx * gy / 2;
+  if ((gx & 1) || (npairs & 7)) {
+    bx = L % gx;
+    by = L / gx;
+    return;
+  }
+  const int P = (L >> 4) * 8 + (L & 7);
+  const int h = (L >> 3) & 1;
+  bx = 2 * (P % (gx / 2)) + h;
+  by = P / (gx / 2);
+}
+
 template <int RB>   // rank blocks of 16: r <= 16 RB
 __global__ __launch_bounds__(256) void merge_adapter_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ absmax8,
@@ -44,8 +63,10 @@ __global__ __launch_bounds__(256) void merge_adapter_kernel(const uint8_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t f0 = (int64_t)blockIdx.y * mg::RT;
-  const int64_t k0 = (int64_t)blockIdx.x * mg::CT;
+  int bx, by;
+  merge_tile(blockIdx.x, (int)((n + mg::CT - 1) / mg::CT), (int)((m + mg::RT - 1) / mg::RT), bx, by);
+  const int64_t f0 = (int64_t)by * mg::RT;
+  const int64_t k0 = (int64_t)bx * mg::CT;
   const int li = lane & 15;
   const int lg = lane >> 4;
 
@@ -157,7 +178,7 @@ __global__ __launch_bounds__(256) void merge_adapter_kernel(const uint8_t* __res
 void launch_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m, int64_t n, int r,
                           float s, const uint16_t* A, const uint16_t* B, uint16_t* out, const Nf4Table& tab,
                           hipStream_t stream) {
-  const dim3 grid((unsigned)((n + mg::CT - 1) / mg::CT), (unsigned)((m + mg::RT - 1) / mg::RT));
+  const dim3 grid((unsigned)(((n + mg::CT - 1) / mg::CT) * ((m + mg::RT - 1) / mg::RT)));
   const int rb = (r + 15) / 16;
   if (rb <= 1)
     hipLaunchKernelGGL(merge_adapter_kernel<1>, grid, dim3(256), 0, stream, codes, absmax8, c2, m, n, r, s, A, B, out, tab);
