@@ -9,6 +9,8 @@ from .api import (  # noqa: F401
     QLORA_OP_BWD,
     QLORA_OP_FWD,
     QuantizedWeight,
+    AdamStep,
+    adam_step,
     alloc_quantized,
     dequant_nf4_dq,
     linear_bwd,

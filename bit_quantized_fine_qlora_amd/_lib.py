@@ -27,6 +27,12 @@ class LinearLayer(ctypes.Structure):
                 ("A", c_vp), ("B", c_vp), ("h", c_vp), ("u_out", c_vp)]
 
 
+class AdamTensor(ctypes.Structure):
+    """qlora_adam_tensor: one adapter tensor of an optimizer step (host struct)."""
+    _fields_ = [("count", c_i64), ("param", c_vp), ("param_bf16", c_vp), ("grad", c_vp),
+                ("exp_avg", c_vp), ("exp_avg_sq", c_vp)]
+
+
 # name -> (restype, argtypes); mirrors include/qlora.h
 PROTOTYPES = {
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -34,6 +40,8 @@ PROTOTYPES = {
     "qlora_nf4_table": (None, [c_vp, c_vp]),
     "qlora_quantize_nf4_dq": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "qlora_dequant_nf4_dq": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "qlora_adam_step": (ctypes.c_int, [ctypes.POINTER(AdamTensor), c_i32, c_f32, c_f32, c_f32, c_f32, c_f32, c_i64,
+                                       c_vp]),
     "qlora_merge_adapter": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp]),
     "qlora_workspace_bytes": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32]),
     "qlora_linear_fwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

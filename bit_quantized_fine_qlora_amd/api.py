@@ -90,6 +90,48 @@ def dequant_nf4_dq(q: QuantizedWeight) -> torch.Tensor:
     return out
 
 
+class AdamStep:
+    """Prepared optimizer step over a fixed list of adapter tensors.
+
+    tensors: list of (param fp32, param_bf16 bf16 or None, grad bf16, exp_avg fp32, exp_avg_sq fp32), each
+    contiguous with the same number of elements, on the GPU or (param and moments) in pinned host memory.
+    The tensor table is marshalled once; run() launches the step.
+    """
+
+    def __init__(self, tensors):
+        self._keep = list(tensors)
+        self._arr = (_lib.AdamTensor * len(self._keep))()
+        self._dev = None
+        for i, (p, p16, g, m, v) in enumerate(self._keep):
+            n = p.numel()
+            if p.dtype != torch.float32 or m.dtype != torch.float32 or v.dtype != torch.float32:
+                raise TypeError("param, exp_avg and exp_avg_sq must be float32")
+            if g.dtype != torch.bfloat16 or (p16 is not None and p16.dtype != torch.bfloat16):
+                raise TypeError("grad and param_bf16 must be bfloat16")
+            named = [(p, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")]
+            if p16 is not None:
+                named.append((p16, "param_bf16"))
+            for t, nm in named:
+                if t.numel() != n or not t.is_contiguous():
+                    raise ValueError(f"{nm}: expected {n} contiguous elements")
+            if g.is_cuda:
+                self._dev = g.device
+            self._arr[i] = _lib.AdamTensor(n, p.data_ptr(), p16.data_ptr() if p16 is not None else None,
+                                           g.data_ptr(), m.data_ptr(), v.data_ptr())
+
+    def run(self, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+            weight_decay: float = 0.0, step: int = 1) -> None:
+        st = _lib.load().qlora_adam_step(self._arr, len(self._keep), float(lr), float(beta1), float(beta2),
+                                         float(eps), float(weight_decay), int(step), _stream(self._dev))
+        _lib.check(st, "qlora_adam_step")
+
+
+def adam_step(tensors, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+              weight_decay: float = 0.0, step: int = 1) -> None:
+    """Adam step with decoupled weight decay on adapter tensors, in place (see AdamStep)."""
+    AdamStep(tensors).run(lr, beta1, beta2, eps, weight_decay, step)
+
+
 def merge_adapter(q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float) -> torch.Tensor:
     """bf16(W' + s B A): the adapter folded into the dequantized weight (m x n bf16)."""
     r = A.shape[0]

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 ROOT = os.path.dirname(PKG_DIR)
 LIB_NAME = "libqlora.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["quantize.hip", "gemm_linear.hip", "gemv_small.hip", "lora.hip", "merge.hip", "api.hip"]
+SOURCES = ["quantize.hip", "gemm_linear.hip", "gemv_small.hip", "lora.hip", "merge.hip", "adam.hip", "api.hip"]
 ARCH = "gfx950"
 
 # No packed-fp32 instructions anywhere; no fast-math (the quantizer's

@@ -48,6 +48,16 @@ void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_
 void launch_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t m, int64_t n, int r,
                           float s, const uint16_t* A, const uint16_t* B, uint16_t* out, const Nf4Table& tab,
                           hipStream_t stream);
+struct AdamTensorHost {
+  int64_t count;
+  float* p;
+  uint16_t* p16;
+  const uint16_t* g;
+  float* m;
+  float* v;
+};
+void launch_adam_step(const AdamTensorHost* ts, int count, float lr, float beta1, float beta2, float eps,
+                      float weight_decay, int64_t step, hipStream_t stream);
 bool gpass_supported(int R);
 int gpass_splits_f(int64_t J, int R);
 int gpass_splits_t(int64_t M);
@@ -318,6 +328,32 @@ qlora_status qlora_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, c
   {
     Timed tm("merge", hs);
     launch_merge_adapter(codes, absmax8, c2, m, n, r, s, A, B, W_out, table(), hs);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, float lr, float beta1, float beta2,
+                             float eps, float weight_decay, int64_t step, qlora_stream_t stream) {
+  if (!tensors) return QLORA_ERR_NULL;
+  if (count < 1) return QLORA_ERR_SHAPE;
+  if (step < 1 || !std::isfinite(lr) || lr < 0.0f || !std::isfinite(eps) || eps < 0.0f ||
+      !std::isfinite(weight_decay) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return QLORA_ERR_VALUE;
+  std::vector<AdamTensorHost> ts((size_t)count);
+  for (int i = 0; i < count; ++i) {
+    const qlora_adam_tensor& t = tensors[i];
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq) return QLORA_ERR_NULL;
+    if (t.count < 1 || t.count >= ((int64_t)1 << 40)) return QLORA_ERR_SHAPE;
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.exp_avg) || !aligned16(t.exp_avg_sq) ||
+        (t.param_bf16 && !aligned16(t.param_bf16)))
+      return QLORA_ERR_ALIGN;
+    ts[(size_t)i] = AdamTensorHost{t.count, t.param, t.param_bf16, t.grad, t.exp_avg, t.exp_avg_sq};
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("adam", hs);
+    for (int i = 0; i < count; i += 64)
+      launch_adam_step(ts.data() + i, count - i < 64 ? count - i : 64, lr, beta1, beta2, eps, weight_decay, step, hs);
   }
   return hip_status();
 }

@@ -122,6 +122,45 @@ qlora_status qlora_merge_adapter(const uint8_t* codes, const uint8_t* absmax8, c
                                  int64_t n, int32_t r, float s, const qlora_bf16* A, const qlora_bf16* B,
                                  qlora_bf16* W_out, qlora_stream_t stream);
 
+/*
+ * One adapter tensor of an optimizer step (host struct; device-addressable
+ * pointers: device memory, or pinned host memory for state kept in CPU RAM).
+ *   count       elements (>= 1).
+ *   param       fp32 master weights, updated in place.
+ *   param_bf16  bf16 copy written after the update (the operand the forward
+ *               and backward read), or NULL.
+ *   grad        bf16 gradient (as qlora_linear_bwd writes it).
+ *   exp_avg, exp_avg_sq  fp32 first and second moments, updated in place
+ *               (zero before the first step).
+ * Every pointer 16-byte aligned.
+ */
+typedef struct {
+  int64_t count;
+  float* param;
+  qlora_bf16* param_bf16;
+  const qlora_bf16* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+} qlora_adam_tensor;
+
+/*
+ * Adam step with decoupled weight decay over `count` adapter tensors in as
+ * few launches as possible (64 tensors per launch).  "QLoRA: Efficient
+ * Fine-Tuning", memory-layout figure (Adam moments for the adapters only,
+ * paged to CPU memory on demand); "What is QLoRA?", Worked example (fp32
+ * parameter, gradient and moments, 16 bytes per trainable parameter);
+ * "QLoRA & 4-bit Fine-Tuning", Innovation 3 (paged optimizer state).  With
+ * t = step (>= 1), per element in fp32:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *   p <- p - (lr / (1 - b1^t)) m / (sqrt(v / (1 - b2^t)) + eps)
+ * (the bias corrections are formed in double on the host).  Requires lr,
+ * eps >= 0 and weight_decay finite, 0 <= beta1, beta2 < 1.  `tensors` is a
+ * host array read before the call returns.  Results match a float64
+ * evaluation of the same step to fp32 rounding.
+ */
+qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, float lr, float beta1, float beta2,
+                             float eps, float weight_decay, int64_t step, qlora_stream_t stream);
+
 /* Operation ids for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1

@@ -31,6 +31,10 @@ What is computed, step by step (numpy; float64 unless a step fixes fp32):
                            chain rule of the forward for grad_x
   adapter merge            [P1] Real-World Impact; [P4] Followups to expect
                            (W' + s B A rounded once to bf16)
+  adapter optimizer step   [P1] memory-layout figure (Adam moments for the
+                           adapters only); [P3] Worked example (fp32 state,
+                           16 bytes per trainable parameter); Adam with
+                           decoupled weight decay
 
 Readings taken where the pages are silent or garbled (each is listed, with
 its reason, in the design notes of the repository):
@@ -388,6 +392,30 @@ def merge_adapter(Wd_bits, A_bits, B_bits, s: float, m: int, n: int) -> np.ndarr
     A = bf16_bits_to_float64(np.asarray(A_bits))
     B = bf16_bits_to_float64(np.asarray(B_bits))
     return bf16_bits_rne_f64(Wd + s * (B @ A)).reshape(m, n)
+
+
+def adam_step(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float):
+    """One Adam step with decoupled weight decay on an adapter tensor, float64.
+
+    [P1] memory-layout figure: Adam moments m, v kept for the adapters only;
+    [P3] "Worked example": fp32 parameter, gradient and the two Adam moments,
+    16 bytes per trainable parameter.  The step is the textbook one:
+      p <- p (1 - lr wd)
+      m <- b1 m + (1 - b1) g            v <- b2 v + (1 - b2) g^2
+      p <- p - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+    with t >= 1 the step number.  Returns (p, m, v); inputs are not modified.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    p = p * (1.0 - lr * weight_decay)
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    p = p - lr * mhat / (np.sqrt(vhat) + eps)
+    return p, m, v
 
 
 def linear_fwd_loops(x, Wd, A, B, s: float):
