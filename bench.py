@@ -20,7 +20,10 @@ events on the stream the library launches on:
   - the adapter optimizer step (Adam, decoupled weight decay) over the
     adapters of a 32-layer 8B-shaped model at r = 16 (448 tensors, 41.9 M
     parameters, 28 bytes each), against the HBM peak, and over one block's
-    adapters with the optimizer state in pinned host memory.
+    adapters with the optimizer state in pinned host memory;
+  - the quantizer on the uniform 4-bit comparison grid: round-trip relative
+    error of the gate weight through the GPU kernels for NF4 and for the
+    uniform grid, and the uniform quantizer's time.
 For the HBM-bound measurements the caches are flushed before every
 repetition by reading 1 GiB (a read evicts the working set cleanly; a write
 flush would leave dirty lines whose write-back lands in the timed kernel).
@@ -158,6 +161,25 @@ def merge_bytes(m, n, r):
     """Packed weight read, adapter read, merged bf16 weight written."""
     numel = m * n
     return numel // 2 + numel // 64 + 4 * ((numel // 64 + 255) // 256) + 2 * (r * n + m * r) + 2 * numel
+
+
+def level_table_variants(Q, W, q, reps):
+    """Round-trip error of the gate weight through quantize + dequant for NF4 and the uniform grid."""
+    import torch
+    w = W.double()
+    out = {}
+    for name, qtype in (("nf4", Q.QTYPE_NF4), ("uniform4", Q.QTYPE_UNIFORM4)):
+        qq = Q.quantize_dq(W, qtype=qtype)
+        d = Q.dequant_dq(qq, qtype=qtype).double()
+        out[name] = {"roundtrip_rel_l2": round(float(torch.linalg.norm(d - w) / torch.linalg.norm(w)), 6)}
+        del qq, d
+    qu = Q.alloc_quantized(q.m, q.n, W.device)
+    med, _ = timed_us(lambda: Q.quantize_dq(W, qtype=Q.QTYPE_UNIFORM4, out=qu), reps)
+    qb = quant_bytes(q.m, q.n)
+    out["uniform4"].update({"quantize_us": round(med, 2), "GB/s": round(qb / (med * 1e-6) / 1e9, 1)})
+    out["workload"] = f"gate weight {q.m}x{q.n}, N(0, 0.02^2)"
+    out["timing"] = "back-to-back launches, no cache flush (the 235 MB weight partly stays in the 256 MB MALL)"
+    return out
 
 
 def adapter_merge(Q, q, A, B, s, reps):
@@ -397,6 +419,7 @@ def main():
     if not args.no_extra:
         out["adapter_merge"] = adapter_merge(Q, q, A, B, s, 10)
         out["adapter_adam"] = adapter_adam(Q, dev, 10)
+        out["level_tables"] = level_table_variants(Q, W, q, 10)
         del W, x, g, A, B, h, gx, ws_f, ws_b
         torch.cuda.empty_cache()
         out["small_tokens"] = small_token_block(Q, dev, 10)

@@ -8,18 +8,23 @@ from .api import (  # noqa: F401
     GroupedForward,
     QLORA_OP_BWD,
     QLORA_OP_FWD,
+    QTYPE_NF4,
+    QTYPE_UNIFORM4,
     QuantizedWeight,
     AdamStep,
     adam_step,
     alloc_quantized,
+    dequant_dq,
     dequant_nf4_dq,
     linear_bwd,
     linear_fwd,
     linear_fwd_grouped,
     merge_adapter,
+    level_table,
     nf4_table,
     profile_enable,
     profile_query,
+    quantize_dq,
     quantize_nf4_dq,
     workspace_bytes,
 )

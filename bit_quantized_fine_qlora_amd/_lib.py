@@ -40,6 +40,9 @@ PROTOTYPES = {
     "qlora_nf4_table": (None, [c_vp, c_vp]),
     "qlora_quantize_nf4_dq": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "qlora_dequant_nf4_dq": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "qlora_level_table": (ctypes.c_int, [c_i32, c_vp, c_vp]),
+    "qlora_quantize_dq": (ctypes.c_int, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "qlora_dequant_dq": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlora_adam_step": (ctypes.c_int, [ctypes.POINTER(AdamTensor), c_i32, c_f32, c_f32, c_f32, c_f32, c_f32, c_i64,
                                        c_vp]),
     "qlora_merge_adapter": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp]),

@@ -50,6 +50,39 @@ def _need(t: torch.Tensor, dtype, shape, name: str):
         raise ValueError(f"{name}: must be contiguous")
 
 
+QTYPE_NF4 = 0
+QTYPE_UNIFORM4 = 1
+
+
+def level_table(qtype: int = QTYPE_NF4):
+    """(levels[16], thresholds[15]) of a level table as the library derived them (host)."""
+    lib = _lib.load()
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _lib.check(lib.qlora_level_table(int(qtype), ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p)),
+               "qlora_level_table")
+    return list(lv), list(th)
+
+
+def quantize_dq(W: torch.Tensor, qtype: int = QTYPE_NF4, out: QuantizedWeight | None = None) -> QuantizedWeight:
+    """Blockwise 4-bit quantization with double quantization on a chosen level table."""
+    m, n = W.shape
+    _need(W, torch.float32, (m, n), "W")
+    q = out if out is not None else alloc_quantized(m, n, W.device)
+    st = _lib.load().qlora_quantize_dq(int(qtype), _ptr(W), m, n, _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2),
+                                       _stream(W.device))
+    _lib.check(st, "qlora_quantize_dq")
+    return q
+
+
+def dequant_dq(q: QuantizedWeight, qtype: int = QTYPE_NF4) -> torch.Tensor:
+    out = torch.empty((q.m, q.n), dtype=torch.bfloat16, device=q.codes.device)
+    st = _lib.load().qlora_dequant_dq(int(qtype), _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2), q.m, q.n, _ptr(out),
+                                      _stream(q.codes.device))
+    _lib.check(st, "qlora_dequant_dq")
+    return out
+
+
 def nf4_table():
     """(levels[16], thresholds[15]) as the library derived them (host)."""
     lib = _lib.load()

@@ -86,11 +86,18 @@ double normal_quantile(double p) {
   return x;
 }
 
-Nf4Table build_table() {
+// 16 levels, symmetric (Q[15 - j] = -Q[j]), and the fp32 midpoints.
+//   qtype 0 (NF4): q_i = Phi^-1((i - 1/2)/16) / q_16
+//   qtype 1 (uniform 4-bit comparison grid): (2j - 15)/15, no zero level
+Nf4Table build_table(int qtype) {
   Nf4Table t;
   double q[16];
-  for (int i = 1; i <= 16; ++i) q[i - 1] = normal_quantile((i - 0.5) / 16.0);
-  for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
+  if (qtype == 0) {
+    for (int i = 1; i <= 16; ++i) q[i - 1] = normal_quantile((i - 0.5) / 16.0);
+    for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
+  } else {
+    for (int j = 0; j < 16; ++j) t.q[j] = (float)((2.0 * j - 15.0) / 15.0);
+  }
   // exact symmetry of the construction, kept exact after rounding
   for (int j = 0; j < 8; ++j) t.q[j] = -t.q[15 - j];
   for (int j = 0; j < 15; ++j) t.t[j] = (float)(((double)t.q[j] + (double)t.q[j + 1]) * 0.5);
@@ -102,7 +109,7 @@ Nf4Table build_table() {
     uint32_t b;
     std::memcpy(&b, &t.t[j], 4);
     if (b < 0x3D800000u || (j > 8 && (b >> 20) == (prev >> 20))) {
-      std::fprintf(stderr, "qlora: NF4 threshold layout breaks the quantizer's interval table\n");
+      std::fprintf(stderr, "qlora: threshold layout breaks the quantizer's interval table\n");
       std::abort();
     }
     prev = b;
@@ -110,8 +117,10 @@ Nf4Table build_table() {
   return t;
 }
 
-const Nf4Table& table() {
-  static const Nf4Table t = build_table();
+const Nf4Table& table(int qtype = 0) {
+  static const Nf4Table u = build_table(1);
+  if (qtype == 1) return u;
+  static const Nf4Table t = build_table(0);
   return t;
 }
 
@@ -282,6 +291,44 @@ void qlora_nf4_table(float* levels, float* thresholds) {
   const Nf4Table& t = table();
   if (levels) std::memcpy(levels, t.q, sizeof(t.q));
   if (thresholds) std::memcpy(thresholds, t.t, sizeof(t.t));
+}
+
+qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds) {
+  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  const Nf4Table& t = table(qtype);
+  if (levels) std::memcpy(levels, t.q, sizeof(t.q));
+  if (thresholds) std::memcpy(thresholds, t.t, sizeof(t.t));
+  return QLORA_OK;
+}
+
+qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t n, uint8_t* codes,
+                               uint8_t* absmax8, float* c2, qlora_stream_t stream) {
+  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  if (!W || !codes || !absmax8 || !c2) return QLORA_ERR_NULL;
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2)) return QLORA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("quantize", s);
+    launch_quantize(W, m * n, codes, absmax8, c2, table(qtype), s);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_dequant_dq(int32_t qtype, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                              int64_t m, int64_t n, qlora_bf16* W_out, qlora_stream_t stream) {
+  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  if (!codes || !absmax8 || !c2 || !W_out) return QLORA_ERR_NULL;
+  qlora_status st = check_weight_shape(m, n);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(W_out)) return QLORA_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("dequant", s);
+    launch_dequant(codes, absmax8, c2, m * n, W_out, table(qtype), s);
+  }
+  return hip_status();
 }
 
 qlora_status qlora_quantize_nf4_dq(const float* W, int64_t m, int64_t n, uint8_t* codes, uint8_t* absmax8,

@@ -161,6 +161,32 @@ typedef struct {
 qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, float lr, float beta1, float beta2,
                              float eps, float weight_decay, int64_t step, qlora_stream_t stream);
 
+/* Level tables for qlora_quantize_dq / qlora_dequant_dq / qlora_level_table. */
+#define QLORA_QTYPE_NF4 0      /* the NF4 levels above */
+#define QLORA_QTYPE_UNIFORM4 1 /* uniform 4-bit grid (2j - 15)/15, j = 0..15 */
+
+/*
+ * The 16 levels and 15 thresholds of a level table (host outputs, either
+ * may be NULL).  QLORA_QTYPE_UNIFORM4 is the plain 4-bit comparison point of
+ * "QLoRA: Efficient Fine-Tuning" Step 1 and "QLoRA & 4-bit Fine-Tuning"
+ * Innovation 1 (NF4 versus uniform 4-bit quantization of normal weights):
+ * 16 evenly spaced levels over [-1, 1] without a zero level, symmetric like
+ * the NF4 table so the same code layout and kernels apply; thresholds are
+ * the fp32 midpoints.  QLORA_ERR_VALUE for an unknown qtype.
+ */
+qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds);
+
+/*
+ * qlora_quantize_nf4_dq / qlora_dequant_nf4_dq with a chosen level table
+ * (qtype 0 gives exactly those calls).  Blocks, double quantization, code
+ * layout, shape rules and errors as there; QLORA_ERR_VALUE for an unknown
+ * qtype.  The linear forward and backward use NF4 only.
+ */
+qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t n, uint8_t* codes,
+                               uint8_t* absmax8, float* c2, qlora_stream_t stream);
+qlora_status qlora_dequant_dq(int32_t qtype, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                              int64_t m, int64_t n, qlora_bf16* W_out, qlora_stream_t stream);
+
 /* Operation ids for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1

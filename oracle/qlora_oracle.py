@@ -106,6 +106,24 @@ def nf4_table():
 NF4_Q, NF4_T = nf4_table()
 
 
+def uniform4_table():
+    """Return (Q, T) of the uniform 4-bit comparison grid: 16 evenly spaced
+    levels spanning [-1, 1] with no zero level, Q_j = fl32((2j - 15) / 15),
+    and the fp32 midpoints T_j as for NF4.
+
+    [P1] Step 1 and [P4] Innovation 1 set NF4 against plain (uniform) 4-bit
+    quantization; this grid is that baseline on the same block absmax
+    normalization, symmetric like the NF4 table so that the same code layout
+    and dequantization apply.
+    """
+    Q = np.array([(2 * j - 15) / 15.0 for j in range(16)], dtype=np.float64).astype(np.float32)
+    T = ((Q[:-1].astype(np.float64) + Q[1:].astype(np.float64)) / 2.0).astype(np.float32)
+    return Q, T
+
+
+UNIFORM4_Q, UNIFORM4_T = uniform4_table()
+
+
 # --------------------------------------------------------------------------
 # The 8-bit float used for the double-quantized constants
 # ([P1] Step 2 "8-bit floats"; [P1] figure "scales stored in FP8";
@@ -208,7 +226,7 @@ def bf16_bits_to_float64(b) -> np.ndarray:
 # Quantizer: blockwise NF4 with double quantization
 # --------------------------------------------------------------------------
 
-def quantize_nf4_dq(W) -> dict:
+def quantize_nf4_dq(W, table=None) -> dict:
     """Quantize a weight matrix (any shape, fp32) in row-major order.
 
     Steps, in the pages' order:
@@ -223,7 +241,10 @@ def quantize_nf4_dq(W) -> dict:
     fewer than 256 blocks.
     Returns dict(codes=uint8[numel/2], absmax8=uint8[numel/64],
                  c2=float32[ceil(numel/16384)], c1=float32[numel/64]).
+    ``table`` = (Q, T) replaces the NF4 levels and thresholds (for example
+    uniform4_table()); everything else is the same.
     """
+    Tt = NF4_T if table is None else table[1]
     w = np.ascontiguousarray(W, dtype=np.float32).reshape(-1)
     if w.size % BLOCK:
         raise ValueError("element count must be a multiple of 64")
@@ -236,7 +257,7 @@ def quantize_nf4_dq(W) -> dict:
     w_hat = (wb / safe[:, None]).astype(np.float32)                         # step 2
     w_hat = np.where(c1[:, None] > 0, w_hat, np.float32(0.0))
     level = np.zeros(wb.shape, dtype=np.uint8)
-    for t in NF4_T:                                                         # step 3
+    for t in Tt:                                                            # step 3
         level += (w_hat > t).astype(np.uint8)
     packed = pack_levels(level.reshape(-1))                                 # step 4
     ngrp = (nblk + DQ_BLOCKS - 1) // DQ_BLOCKS
@@ -293,7 +314,7 @@ def block_scales(absmax8, c2, nblk: int) -> np.ndarray:
     return (dec * c2_of_block).astype(np.float32)
 
 
-def dequant_nf4_dq(codes, absmax8, c2, numel: int, first_element: int = 0) -> np.ndarray:
+def dequant_nf4_dq(codes, absmax8, c2, numel: int, first_element: int = 0, table=None) -> np.ndarray:
     """bf16 bit patterns of W' = bf16(fl32(Q[code] * s_b)).
 
     [P1] Step 3 symbols: W0 is dequantized to BF16 at run time.
@@ -308,7 +329,8 @@ def dequant_nf4_dq(codes, absmax8, c2, numel: int, first_element: int = 0) -> np
     grp = (b0 + np.arange(nblk)) // DQ_BLOCKS
     dec = e4m3_decode(np.asarray(absmax8)[:nblk]).astype(np.float32)
     s = (dec * np.asarray(c2, dtype=np.float32)[grp]).astype(np.float32)
-    q = NF4_Q[unpack_codes(codes, numel)].reshape(nblk, BLOCK)
+    Qt = NF4_Q if table is None else table[0]
+    q = Qt[unpack_codes(codes, numel)].reshape(nblk, BLOCK)
     vals = (q * s[:, None]).astype(np.float32)
     return bf16_bits_rne(vals.reshape(-1))
 

@@ -51,6 +51,16 @@ def test_library_table_matches_oracle(lib):
     assert np.array_equal(got_t.view(np.uint32), O.NF4_T.view(np.uint32))
 
 
+def test_level_tables_match_oracle(lib):
+    for qtype, (Q, T) in ((0, (O.NF4_Q, O.NF4_T)), (1, (O.UNIFORM4_Q, O.UNIFORM4_T))):
+        lv = (ctypes.c_float * 16)()
+        th = (ctypes.c_float * 15)()
+        assert lib.qlora_level_table(qtype, ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p)) == 0
+        assert np.array_equal(np.frombuffer(lv, dtype=np.float32).view(np.uint32), Q.view(np.uint32)), qtype
+        assert np.array_equal(np.frombuffer(th, dtype=np.float32).view(np.uint32), T.view(np.uint32)), qtype
+    assert lib.qlora_level_table(2, None, None) == -7
+
+
 def test_status_strings(lib):
     for st in range(-7, 1):
         assert len(lib.qlora_status_string(st)) >= 2
@@ -70,6 +80,14 @@ def test_quantize_argument_errors(lib):
     assert f(P, 4, 0, P, P, P, None) == -2
     assert f(MIS, 4, 64, P, P, P, None) == -4
     assert f(P, 1 << 31, 64, P, P, P, None) == -2
+
+
+def test_level_table_variant_argument_errors(lib):
+    assert lib.qlora_quantize_dq(5, P, 4, 64, P, P, P, None) == -7
+    assert lib.qlora_quantize_dq(1, P, 4, 60, P, P, P, None) == -2
+    assert lib.qlora_quantize_dq(1, None, 4, 64, P, P, P, None) == -1
+    assert lib.qlora_dequant_dq(-1, P, P, P, 4, 64, P, None) == -7
+    assert lib.qlora_dequant_dq(1, P, P, P, 4, 64, MIS, None) == -4
 
 
 def test_dequant_argument_errors(lib):

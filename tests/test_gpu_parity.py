@@ -307,6 +307,38 @@ def test_quantizer_threshold_boundaries(Q):
     check_quantizer(q, O.quantize_nf4_dq(W))
 
 
+# ------------------------------------------------------------------ uniform 4-bit grid
+
+UNIFORM4 = [(64, 256), (333, 192), (14336, 4096)]
+
+
+@pytest.mark.parametrize("m,n", UNIFORM4)
+def test_uniform4_quantizer(Q, m, n):
+    # the comparison grid through the same quantizer and dequantizer: bit-exact
+    inp = QI.custom_inputs(seed=m + 2 * n, M=1, n=n, m=m, r=1)
+    W = inp["W"]
+    table = O.uniform4_table()
+    say(f"uniform4 quantize {m}x{n}")
+    q = Q.quantize_dq(torch.from_numpy(W).cuda(), qtype=Q.QTYPE_UNIFORM4)
+    torch.cuda.synchronize()
+    qw = O.quantize_nf4_dq(W, table=table)
+    check_quantizer(q, qw)
+    deq = host_bits(Q.dequant_dq(q, qtype=Q.QTYPE_UNIFORM4)).reshape(-1)
+    want = O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table)
+    assert np.array_equal(deq, want), "uniform4 dequantized weight differs"
+    if m * n >= 1 << 20:
+        # the pages' claim with the GPU kernels: NF4 round trip beats the uniform grid
+        w64 = W.reshape(-1).astype(np.float64)
+        qn = Q.quantize_dq(torch.from_numpy(W).cuda(), qtype=Q.QTYPE_NF4)
+        e_nf4 = np.linalg.norm(f64(host_bits(Q.dequant_dq(qn)).reshape(-1)) - w64) / np.linalg.norm(w64)
+        e_uni = np.linalg.norm(f64(deq) - w64) / np.linalg.norm(w64)
+        say(f"round-trip rel-L2: nf4 {e_nf4:.5f}, uniform4 {e_uni:.5f}")
+        assert e_nf4 < e_uni
+        del qn
+    del q
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ adapter merge
 
 def bf16_order(bits):

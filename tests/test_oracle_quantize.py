@@ -18,12 +18,12 @@ from oracle import qlora_oracle as O
 import qlora_inputs as QI
 
 
-def brute_nearest_codes(w):
+def brute_nearest_codes(w, Q=None):
     """argmin_j |w/c1 - Q_j| in float64 per element, ties to the lower code."""
     wb = np.asarray(w, dtype=np.float32).reshape(-1, 64)
     c1 = np.max(np.abs(wb), axis=1)
     out = np.empty(wb.shape, dtype=np.int64)
-    Q = O.NF4_Q.astype(np.float64)
+    Q = (O.NF4_Q if Q is None else Q).astype(np.float64)
     for b in range(wb.shape[0]):
         for e in range(64):
             what = 0.0 if c1[b] == 0 else float(np.float32(wb[b, e]) / np.float32(c1[b]))
@@ -260,3 +260,50 @@ def test_packing_order_and_roundtrip():
         for j in range(4):
             b = int(packed[4 * g + j])
             assert b & 0xF == codes[8 * g + j] and b >> 4 == codes[8 * g + j + 4]
+
+
+# ------------------------------------------------------------ uniform 4-bit grid
+
+def test_uniform4_table_closed_form():
+    Q, T = O.uniform4_table()
+    for j in range(16):
+        assert Q[j] == np.float32((2 * j - 15) / 15.0)
+        assert Q[15 - j] == -Q[j]
+    assert np.all(np.diff(Q.astype(np.float64)) > 0)
+    assert T[7] == 0.0
+    for j in range(15):
+        assert T[j] == np.float32((float(Q[j]) + float(Q[j + 1])) / 2.0)
+    # the spacing is uniform to fp32 rounding
+    assert np.allclose(np.diff(Q.astype(np.float64)), 2.0 / 15.0, rtol=0, atol=1e-7)
+
+
+def test_uniform4_threshold_rule_equals_nearest_level():
+    rng = np.random.default_rng(6)
+    W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    qw = O.quantize_nf4_dq(W, table=O.uniform4_table())
+    got = O.unpack_codes(qw["codes"], W.size).astype(np.int64)
+    want = brute_nearest_codes(W, O.UNIFORM4_Q)
+    diff = np.nonzero(got != want)[0]
+    wb = W.reshape(-1)
+    c1 = np.repeat(qw["c1"], 64)
+    for i in diff:
+        what = np.float32(wb[i]) / np.float32(c1[i])
+        assert np.min(np.abs(O.UNIFORM4_T.astype(np.float64) - float(what))) <= float(np.spacing(np.float32(what)))
+    assert len(diff) <= 2
+
+
+def test_uniform4_error_above_nf4_and_near_int4():
+    # the uniform grid through the same pipeline (double quant, bf16) loses to
+    # NF4 on normal weights, and lands near the 15-level INT4 absmax round trip
+    rng = np.random.default_rng(15)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+    w64 = W.reshape(-1).astype(np.float64)
+    rel = lambda a: np.linalg.norm(a - w64) / np.linalg.norm(w64)  # noqa: E731
+    errs = {}
+    for name, table in (("nf4", None), ("uniform4", O.uniform4_table())):
+        qw = O.quantize_nf4_dq(W, table=table)
+        deq = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table))
+        errs[name] = rel(deq)
+    assert errs["nf4"] < errs["uniform4"]
+    e_int4 = rel(O.int4_absmax_roundtrip(W))
+    assert abs(errs["uniform4"] - e_int4) < 0.25 * e_int4
