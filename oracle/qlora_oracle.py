@@ -31,6 +31,9 @@ What is computed, step by step (numpy; float64 unless a step fixes fp32):
                            chain rule of the forward for grad_x
   adapter merge            [P1] Real-World Impact; [P4] Followups to expect
                            (W' + s B A rounded once to bf16)
+  LoRA dropout             [P1] LoraConfig snippet (lora_dropout) on the
+                           adapter input; mask from Philox4x32-10 (counter-
+                           based, published definition)
   adapter optimizer step   [P1] memory-layout figure (Adam moments for the
                            adapters only); [P3] Worked example (fp32 state,
                            16 bytes per trainable parameter); Adam with
@@ -438,6 +441,87 @@ def adam_step(p, g, m, v, t: int, lr: float, beta1: float, beta2: float, eps: fl
     vhat = v / (1.0 - beta2 ** t)
     p = p - lr * mhat / (np.sqrt(vhat) + eps)
     return p, m, v
+
+
+# --------------------------------------------------------------------------
+# LoRA dropout on the adapter input (the snippet's lora_dropout)
+# --------------------------------------------------------------------------
+
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57   # round multipliers
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85   # key schedule increments
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw: "Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011), in Python integers.
+
+    ctr: four 32-bit words, key: two.  A round multiplies counter words 0 and
+    2 by the two constants (64-bit products split into high and low halves),
+    then permutes and mixes: (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3
+    ^ k1, lo(M0 c0)); the key gets the Weyl increments between rounds.
+    """
+    c = [int(v) & 0xFFFFFFFF for v in ctr]
+    k = [int(v) & 0xFFFFFFFF for v in key]
+    for r in range(10):
+        if r:
+            k = [(k[0] + PHILOX_W0) & 0xFFFFFFFF, (k[1] + PHILOX_W1) & 0xFFFFFFFF]
+        p0 = PHILOX_M0 * c[0]
+        p1 = PHILOX_M1 * c[2]
+        c = [((p1 >> 32) ^ c[1] ^ k[0]) & 0xFFFFFFFF, p1 & 0xFFFFFFFF,
+             ((p0 >> 32) ^ c[3] ^ k[1]) & 0xFFFFFFFF, p0 & 0xFFFFFFFF]
+    return c
+
+
+def dropout_keep_threshold(p: float) -> int:
+    """32-bit threshold: an element is dropped when its random word is below it."""
+    return min(int(round(p * 2.0 ** 32)), 0xFFFFFFFF)
+
+
+def dropout_mask(M: int, n: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """Keep-mask (bool, M x n) of the adapter input.
+
+    Element e = t n + k takes word e % 4 of Philox4x32-10 at the 64-bit
+    counter e // 4 + offset (low word first, upper two words zero) under the
+    key (seed low 32 bits, seed high 32 bits); it is kept when that word is
+    at least round(p 2^32).  [P1] LoraConfig snippet (lora_dropout), applied
+    to the input of the adapter branch only.
+    """
+    thr = dropout_keep_threshold(p)
+    key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    total = M * n
+    words = np.empty(((total + 3) // 4) * 4, dtype=np.uint64)
+    for c in range((total + 3) // 4):
+        ctr = c + offset
+        words[4 * c:4 * c + 4] = philox4x32_10((ctr & 0xFFFFFFFF, (ctr >> 32) & 0xFFFFFFFF, 0, 0), key)
+    return (words[:total] >= thr).reshape(M, n)
+
+
+def linear_fwd_dropout(x, Wd, A, B, s: float, keep, p: float):
+    """Forward with dropout on the adapter input: u = (x * keep / (1 - p)) A^T,
+    h = x W'^T + s u B^T.  [P1] Step 3, Eq. 3 and the snippet's lora_dropout."""
+    x = np.asarray(x, dtype=np.float64)
+    xd = x * np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    u = xd @ np.asarray(A, dtype=np.float64).T
+    h = x @ np.asarray(Wd, dtype=np.float64).T + s * (u @ np.asarray(B, dtype=np.float64).T)
+    return h, u
+
+
+def linear_bwd_dropout(x, g, Wd, A, B, s: float, keep, p: float):
+    """Gradients of <g, h> for linear_fwd_dropout (chain rule; the mask is fixed):
+    v = g B, grad_x = g W' + s (v A) * keep / (1 - p),
+    grad_A = s v^T (x * keep / (1 - p)), grad_B = s g^T u."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    kf = np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    xd = x * kf
+    u = xd @ A.T
+    v = g @ B
+    grad_x = g @ np.asarray(Wd, dtype=np.float64) + s * (v @ A) * kf
+    grad_A = s * (v.T @ xd)
+    grad_B = s * (g.T @ u)
+    return dict(grad_x=grad_x, grad_A=grad_A, grad_B=grad_B, v=v, u=u)
 
 
 def linear_fwd_loops(x, Wd, A, B, s: float):
