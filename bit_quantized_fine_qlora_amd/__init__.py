@@ -7,6 +7,7 @@ include/qlora.h); this package is a thin torch binding over it.
 from .api import (  # noqa: F401
     GroupedForward,
     QLORA_OP_BWD,
+    QLORA_OP_BWD_DROPOUT,
     QLORA_OP_FWD,
     QTYPE_NF4,
     QTYPE_UNIFORM4,

@@ -27,6 +27,11 @@ class LinearLayer(ctypes.Structure):
                 ("A", c_vp), ("B", c_vp), ("h", c_vp), ("u_out", c_vp)]
 
 
+class Dropout(ctypes.Structure):
+    """qlora_dropout: dropout on the adapter input (host struct)."""
+    _fields_ = [("p", c_f32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
+
+
 class AdamTensor(ctypes.Structure):
     """qlora_adam_tensor: one adapter tensor of an optimizer step (host struct)."""
     _fields_ = [("count", c_i64), ("param", c_vp), ("param_bf16", c_vp), ("grad", c_vp),
@@ -53,6 +58,11 @@ PROTOTYPES = {
     "qlora_linear_fwd_grouped": (ctypes.c_int, [c_i64, c_i32, ctypes.POINTER(LinearLayer), c_vp, c_sz, c_vp]),
     "qlora_linear_bwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qlora_linear_fwd_ex": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, ctypes.POINTER(Dropout), c_vp, c_sz, c_vp]),
+    "qlora_linear_bwd_ex": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(Dropout), c_vp, c_sz,
+                                           c_vp]),
     "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "qlora_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
 }

@@ -16,6 +16,7 @@ from . import _lib
 
 QLORA_OP_FWD = 0
 QLORA_OP_BWD = 1
+QLORA_OP_BWD_DROPOUT = 2
 
 
 @dataclasses.dataclass
@@ -184,10 +185,22 @@ def _workspace(op, M, n, m, r, device, workspace):
     return workspace
 
 
+def _dropout(dropout):
+    """(p, seed, offset) or None -> a qlora_dropout pointer (None: plain layer)."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    return ctypes.pointer(_lib.Dropout(float(p), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1)))
+
+
 def linear_fwd(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
                h: torch.Tensor | None = None, u: torch.Tensor | None = None, want_u: bool = True,
-               workspace: torch.Tensor | None = None):
-    """h = x W'^T + s (x A^T) B^T.  Returns (h bf16 [M, m], u fp32 [M, r] or None)."""
+               workspace: torch.Tensor | None = None, dropout=None):
+    """h = x W'^T + s (x A^T) B^T.  Returns (h bf16 [M, m], u fp32 [M, r] or None).
+
+    dropout: (p, seed, offset) for dropout on the adapter input (the adapter
+    reads x * keep / (1 - p)), or None.
+    """
     M, n = x.shape
     m = q.m
     r = A.shape[0]
@@ -199,9 +212,16 @@ def linear_fwd(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Te
     if u is None and want_u:
         u = torch.empty((M, r), dtype=torch.float32, device=x.device)
     ws = _workspace(QLORA_OP_FWD, M, n, m, r, x.device, workspace)
-    st = _lib.load().qlora_linear_fwd(M, n, m, r, float(s), _ptr(x), _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2),
-                                      _ptr(A), _ptr(B), _ptr(h), _ptr(u), _ptr(ws), ws.numel(), _stream(x.device))
-    _lib.check(st, "qlora_linear_fwd")
+    if dropout is None:
+        st = _lib.load().qlora_linear_fwd(M, n, m, r, float(s), _ptr(x), _ptr(q.codes), _ptr(q.absmax8),
+                                          _ptr(q.c2), _ptr(A), _ptr(B), _ptr(h), _ptr(u), _ptr(ws), ws.numel(),
+                                          _stream(x.device))
+        _lib.check(st, "qlora_linear_fwd")
+    else:
+        st = _lib.load().qlora_linear_fwd_ex(M, n, m, r, float(s), _ptr(x), _ptr(q.codes), _ptr(q.absmax8),
+                                             _ptr(q.c2), _ptr(A), _ptr(B), _ptr(h), _ptr(u), _dropout(dropout),
+                                             _ptr(ws), ws.numel(), _stream(x.device))
+        _lib.check(st, "qlora_linear_fwd_ex")
     return h, u
 
 
@@ -257,8 +277,12 @@ def linear_fwd_grouped(layers):
 
 def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
                u: torch.Tensor | None = None, need_grad_x: bool = True, out=None,
-               workspace: torch.Tensor | None = None):
-    """Returns (grad_x bf16 [M, n] or None, grad_A bf16 [r, n], grad_B bf16 [m, r])."""
+               workspace: torch.Tensor | None = None, dropout=None):
+    """Returns (grad_x bf16 [M, n] or None, grad_A bf16 [r, n], grad_B bf16 [m, r]).
+
+    dropout: the forward's (p, seed, offset), or None; u, when given, is the
+    forward's u (with the mask).
+    """
     M, n = x.shape
     m = q.m
     r = A.shape[0]
@@ -274,11 +298,19 @@ def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Te
         gB = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
     else:
         gx, gA, gB = out
-    ws = _workspace(QLORA_OP_BWD, M, n, m, r, x.device, workspace)
-    st = _lib.load().qlora_linear_bwd(M, n, m, r, float(s), _ptr(x), _ptr(g), _ptr(q.codes), _ptr(q.absmax8),
-                                      _ptr(q.c2), _ptr(A), _ptr(B), _ptr(u), _ptr(gx), _ptr(gA), _ptr(gB), _ptr(ws),
-                                      ws.numel(), _stream(x.device))
-    _lib.check(st, "qlora_linear_bwd")
+    if dropout is None:
+        ws = _workspace(QLORA_OP_BWD, M, n, m, r, x.device, workspace)
+        st = _lib.load().qlora_linear_bwd(M, n, m, r, float(s), _ptr(x), _ptr(g), _ptr(q.codes), _ptr(q.absmax8),
+                                          _ptr(q.c2), _ptr(A), _ptr(B), _ptr(u), _ptr(gx), _ptr(gA), _ptr(gB),
+                                          _ptr(ws), ws.numel(), _stream(x.device))
+        _lib.check(st, "qlora_linear_bwd")
+    else:
+        ws = _workspace(QLORA_OP_BWD_DROPOUT, M, n, m, r, x.device, workspace)
+        st = _lib.load().qlora_linear_bwd_ex(M, n, m, r, float(s), _ptr(x), _ptr(g), _ptr(q.codes),
+                                             _ptr(q.absmax8), _ptr(q.c2), _ptr(A), _ptr(B), _ptr(u), _ptr(gx),
+                                             _ptr(gA), _ptr(gB), _dropout(dropout), _ptr(ws), ws.numel(),
+                                             _stream(x.device))
+        _lib.check(st, "qlora_linear_bwd_ex")
     return gx, gA, gB
 
 

@@ -24,7 +24,8 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
-                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream);
+                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream,
+                       const float* add);
 int small_max_tokens();
 int small_max_layers();
 size_t small_ws_bytes(int64_t M, int64_t n, int64_t m, int r);
@@ -33,14 +34,19 @@ struct SmallLayerHost {
   const uint16_t* A; const uint16_t* B; uint16_t* h; float* u_out;
   int64_t n, m; int r; float s;
   void* ws;
+  DropoutDev drop{};
+  float u_scale = 1.0f;
 };
 void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4Table& tab, hipStream_t stream);
 int down_proj_splits(int64_t M, int64_t K, int R);
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
-                      float* out, hipStream_t stream);
+                      float* out, hipStream_t stream, const DropoutDev* drop, float scale);
 int token_grad_splits(int64_t M, int64_t J, int R);
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
-                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream);
+                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
+                       const DropoutDev* drop);
+void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
+                              const DropoutDev& drop, float* out, hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
@@ -227,13 +233,13 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, total;
   int su, sv, sa, sb;
   bool gpass;     // v and grad_B from one read of g
   int64_t m_pad;  // row length of g as the kernels read it
 };
 
-BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
+BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   WsLayout L;
   BwdWs w;
   // The kernels read g in 16-byte pieces; rows whose length is not a
@@ -255,8 +261,28 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
   w.gB = w.gpass ? 0 : L.take((size_t)w.sb * w.m_pad * r * sizeof(float));
   w.vpart = w.gpass ? L.take((size_t)gpass_splits_f(w.m_pad, r) * M * r * sizeof(float)) : 0;
   w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
+  // dropout: the masked adapter part of grad_x in fp32
+  w.dterm = dropout ? L.take((size_t)M * n * sizeof(float)) : 0;
   w.total = L.total;
   return w;
+}
+
+// Device form of a dropout request; inv_keep = 1 / (1 - p).  NULL or p = 0
+// leaves the mask off.
+qlora_status make_dropout(const qlora_dropout* d, DropoutDev& out, float& inv_keep) {
+  out = DropoutDev{0u, 0u, 0u, 0ull, 0};
+  inv_keep = 1.0f;
+  if (!d) return QLORA_OK;
+  if (!std::isfinite(d->p) || d->p < 0.0f || d->p >= 1.0f) return QLORA_ERR_VALUE;
+  if (d->p == 0.0f) return QLORA_OK;
+  const double t = std::nearbyint((double)d->p * 4294967296.0);  // ties to even
+  out.thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  out.k0 = (uint32_t)(d->seed & 0xFFFFFFFFull);
+  out.k1 = (uint32_t)(d->seed >> 32);
+  out.offset = d->offset;
+  out.on = 1;
+  inv_keep = (float)(1.0 / (1.0 - (double)d->p));
+  return QLORA_OK;
 }
 
 template <typename T>
@@ -409,6 +435,7 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r)
   if (check_linear(M, n, m, r, 1.0f) != QLORA_OK) return 0;
   if (op == QLORA_OP_FWD) return fwd_ws(M, n, m, r).total;
   if (op == QLORA_OP_BWD) return bwd_ws(M, n, m, r).total;
+  if (op == QLORA_OP_BWD_DROPOUT) return bwd_ws(M, n, m, r, true).total;
   return 0;
 }
 
@@ -416,7 +443,20 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
                               const uint8_t* codes, const uint8_t* absmax8, const float* c2, const qlora_bf16* A,
                               const qlora_bf16* B, qlora_bf16* h, float* u_out, void* workspace,
                               size_t workspace_bytes, qlora_stream_t stream) {
+  return qlora_linear_fwd_ex(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out, nullptr, workspace,
+                             workspace_bytes, stream);
+}
+
+qlora_status qlora_linear_fwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                 const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                 const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
+                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
+                                 qlora_stream_t stream) {
   qlora_status st = check_linear(M, n, m, r, s);
+  if (st != QLORA_OK) return st;
+  DropoutDev dd;
+  float inv_keep;
+  st = make_dropout(dropout, dd, inv_keep);
   if (st != QLORA_OK) return st;
   if (!x || !codes || !absmax8 || !c2 || !A || !B || !h) return QLORA_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(A) ||
@@ -427,7 +467,9 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (M <= small_max_tokens()) {
-    const SmallLayerHost L{x, codes, absmax8, c2, A, B, h, u_out, n, m, r, s, workspace};
+    SmallLayerHost L{x, codes, absmax8, c2, A, B, h, u_out, n, m, r, s, workspace};
+    L.drop = dd;
+    L.u_scale = inv_keep;
     Timed tm("fwd_small", hs);
     launch_small_fwd((int)M, &L, 1, table(), hs);
     return hip_status();
@@ -435,7 +477,7 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   float* u = u_out ? u_out : at<float>(workspace, w.u);
   {
     Timed tm("down_proj", hs);
-    launch_down_proj(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs);
+    launch_down_proj(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs, &dd, inv_keep);
   }
   {
     Timed tm("fwd_gemm", hs);
@@ -509,14 +551,29 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
                               const qlora_bf16* A, const qlora_bf16* B, const float* u, qlora_bf16* grad_x,
                               qlora_bf16* grad_A, qlora_bf16* grad_B, void* workspace, size_t workspace_bytes,
                               qlora_stream_t stream) {
+  return qlora_linear_bwd_ex(M, n, m, r, s, x, g, codes, absmax8, c2, A, B, u, grad_x, grad_A, grad_B, nullptr,
+                             workspace, workspace_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                 const qlora_bf16* g, const uint8_t* codes, const uint8_t* absmax8,
+                                 const float* c2, const qlora_bf16* A, const qlora_bf16* B, const float* u,
+                                 qlora_bf16* grad_x, qlora_bf16* grad_A, qlora_bf16* grad_B,
+                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
+                                 qlora_stream_t stream) {
   qlora_status st = check_linear(M, n, m, r, s);
   if (st != QLORA_OK) return st;
+  DropoutDev dd;
+  float inv_keep;
+  st = make_dropout(dropout, dd, inv_keep);
+  if (st != QLORA_OK) return st;
+  const bool drop = dd.on != 0;
   if (!x || !g || !codes || !absmax8 || !c2 || !A || !B || !grad_A || !grad_B) return QLORA_ERR_NULL;
   if (!aligned16(x) || !aligned16(g) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) ||
       !aligned16(A) || !aligned16(B) || !aligned16(grad_A) || !aligned16(grad_B) || (u && !aligned16(u)) ||
       (grad_x && !aligned16(grad_x)))
     return QLORA_ERR_ALIGN;
-  const BwdWs w = bwd_ws(M, n, m, r);
+  const BwdWs w = bwd_ws(M, n, m, r, drop);
   if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -532,7 +589,7 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
   const float* uu = u;
   if (!uu) {
     Timed tm("down_proj", hs);
-    launch_down_proj(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs);
+    launch_down_proj(x, M, n, A, r, part, w.su, at<float>(workspace, w.u), hs, &dd, inv_keep);
     uu = at<float>(workspace, w.u);
   }
   float* v = at<float>(workspace, w.v);
@@ -549,20 +606,34 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
     }
     {
       Timed tm("down_proj", hs);
-      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs);
+      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs, nullptr, 1.0f);
     }
     {
       Timed tm("token_grad", hs);
-      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs);
+      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr);
     }
   }
   {
     Timed tm("token_grad", hs);
-    launch_token_grad(x, M, n, n, v, r, s, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs);
+    // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p)
+    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd);
   }
   if (grad_x) {
-    Timed tm("dgrad_gemm", hs);
-    launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, nullptr, table(), hs);
+    if (drop) {
+      // the adapter part s (v A) * keep / (1 - p) in fp32; the GEMM adds it
+      // to g W' before rounding and runs no LoRA steps of its own
+      float* dterm = at<float>(workspace, w.dterm);
+      {
+        Timed tm("dropout_term", hs);
+        launch_lora_dropout_term(v, A, M, n, r, s * inv_keep, dd, dterm, hs);
+      }
+      Timed tm("dgrad_gemm", hs);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, 0, s, nullptr, table(), hs, dterm);
+    } else {
+      Timed tm("dgrad_gemm", hs);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, nullptr, table(), hs,
+                        nullptr);
+    }
   }
   return hip_status();
 }

@@ -92,6 +92,7 @@ struct GemmArgs {
   int nsplit;
   float* partial;         // nsplit x 256 x 256 fp32, the first finisher's sum
   uint32_t* split_sync;   // nsplit x {arrivals, partial ready}, zero at launch
+  const float* add;       // M x N fp32 added before the rounding, or null
 };
 
 // The two halves of a split tile meet at the end: the first to finish
@@ -457,6 +458,23 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
       }
     }
   }
+  if (p.add) {
+    // an fp32 term of the output computed elsewhere, added once per tile
+    // before the single rounding (M N 4 < 2^32 bytes; rows past M read 0)
+    const uint32_t add_bytes = (uint32_t)(p.M * p.N * 4);
+    const brsrc_t r_add = make_rsrc(p.add, add_bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t t = t0 + wt + 16 * j + lr;
+        const int64_t f = f0 + wf + 16 * i + 4 * lq;
+        const bool ok = t < p.M && f < p.N;
+        acc[i][j] += __builtin_bit_cast(f32x4, bload128(r_add, ok ? (uint32_t)((t * p.N + f) * 4) : add_bytes));
+        asm volatile("" : "+v"(acc[i][j]));
+      }
+    }
+  }
 
   // ---- store (bf16) through LDS, so that global writes are whole rows ----
   // The K loop's last barrier has freed all tiles.  Each wave stages its
@@ -611,11 +629,14 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 
 // g is M x m_pad (m_pad = m, or m rounded up to 64 with zero columns when
 // m % 8 != 0, so every 16-byte chunk of the tensor is whole).
+// add: M x n fp32 added to the result before its rounding, or null; r = 0
+// runs no LoRA steps.
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
-                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream) {
+                       int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream,
+                       const float* add) {
   GemmArgs p{};
-  p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = A; p.lora_b = v; p.out = gx;
+  p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = A; p.lora_b = v; p.out = gx; p.add = add;
   p.M = M; p.K = m_pad; p.N = n; p.wn = n; p.wm = m; p.r = r; p.s = s;
   launch_linear_gemm(true, p, split_ws, tab, stream);
 }

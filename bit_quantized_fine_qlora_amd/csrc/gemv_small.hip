@@ -66,6 +66,8 @@ struct SmallLayer {
   int wg_begin;             // first workgroup of this layer in the launch
   int u_begin;              // first u workgroup of this layer (after all dequantizing ones)
   int64_t out_begin;        // first finishing workgroup of this layer
+  DropoutDev drop;          // dropout on x as the adapter reads it
+  float u_scale;            // u = u_scale * (masked x) A^T: 1 / (1 - p), or 1
 };
 
 struct SmallArgs {
@@ -121,7 +123,9 @@ __device__ void small_u_chunk(const SmallArgs& a, uint8_t* lds, f32x4* ured) {
   for (int t = 0; t < MP; ++t) {
     const int64_t k = k0 + kq + 8 * lane;
     const bool ok = t < M && k < K;
-    *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
+    u32x4 w = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
+    if (Ly.drop.on && ok) w = dropout8(Ly.drop, (uint64_t)((int64_t)t * K + k), w);  // element t K + k
+    *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = w;
   }
   const uint32_t arbytes = (uint32_t)((int64_t)r * K * 2);
   const brsrc_t ra = make_rsrc(Ly.A, arbytes);
@@ -409,6 +413,8 @@ __device__ void small_reduce_aligned(const SmallLayer& Ly, int tile, int M) {
           u0 += __builtin_bit_cast(f32x4, w0[c]);
           u1 += __builtin_bit_cast(f32x4, w1[c]);
         }
+      u0 *= Ly.u_scale;
+      u1 *= Ly.u_scale;
       if (Ly.u_out && tile == 0 && wave == 0 && tv && q0 < r) {
         *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0) = u0;
         *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0 + 4) = u1;
@@ -461,6 +467,8 @@ __device__ void small_reduce_aligned(const SmallLayer& Ly, int tile, int M) {
             u1 += __builtin_bit_cast(f32x4, w1[c]);
           }
       }
+      u0 *= Ly.u_scale;
+      u1 *= Ly.u_scale;
       if (Ly.u_out && tile == 0 && wave == 0 && qv) {
         *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0) = u0;
         *reinterpret_cast<f32x4*>(Ly.u_out + (int64_t)t * r + q0 + 4) = u1;
@@ -510,6 +518,7 @@ __global__ __launch_bounds__(256) void small_reduce_kernel(SmallArgs a) {
       for (int c = 0; c < 8; ++c)
         if (c0 + c < nparts) uq += v[c];
     }
+    uq *= Ly.u_scale;
     su[idx] = uq;
     if (Ly.u_out && tile == 0) Ly.u_out[idx] = uq;
   }
@@ -611,6 +620,8 @@ struct SmallLayerHost {
   const uint16_t* A; const uint16_t* B; uint16_t* h; float* u_out;
   int64_t n, m; int r; float s;
   void* ws;  // small_ws_bytes(M, n, m, r) bytes, 256-aligned
+  DropoutDev drop{};     // off unless set
+  float u_scale = 1.0f;  // applied to u after the chunk sum
 };
 
 void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4Table& tab, hipStream_t stream) {
@@ -635,6 +646,7 @@ void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4T
     SmallLayer& L = a.L[i];
     L.x = h.x; L.codes = h.codes; L.absmax8 = h.absmax8; L.c2 = h.c2; L.A = h.A; L.B = h.B; L.h = h.h;
     L.u_out = h.u_out; L.n = h.n; L.m = h.m; L.r = h.r; L.s = h.s;
+    L.drop = h.drop; L.u_scale = h.u_scale;
     L.nkc = (int)small_nkc(h.n);
     L.fbw = fbw;
     L.ngroups = (int)cdiv_s(cdiv_s(h.m, 16), fbw);

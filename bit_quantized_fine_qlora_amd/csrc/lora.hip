@@ -40,7 +40,7 @@ constexpr int XB = TT * 256;  // X tile bytes per stage
 template <int RB>
 __global__ __launch_bounds__(256) void down_proj_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         const uint16_t* __restrict__ Y, int R,
-                                                        float* __restrict__ part, int64_t kc) {
+                                                        float* __restrict__ part, int64_t kc, DropoutDev drop) {
   constexpr int YB = RB * 16 * 256;
   constexpr int STAGE = dp::XB + YB;
   __shared__ __align__(16) uint8_t lds[2 * STAGE];
@@ -81,10 +81,15 @@ __global__ __launch_bounds__(256) void down_proj_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < RB; ++i) yr[i] = bload128(ry, ok ? yo[i] + d : ybytes);
   };
-  auto store = [&](int buf, const u32x4(&xr)[4], const u32x4(&yr)[RB]) {
+  // dropout (adapter input only): X element (t, k) is e = t K + k
+  auto store = [&](int buf, int st, const u32x4(&xr)[4], const u32x4(&yr)[RB]) {
     uint8_t* base = lds + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + sw256(16 * i + prow, pc)) = xr[i];
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w = xr[i];
+      if (drop.on) w = dropout8(drop, (uint64_t)((t0 + 16 * i + prow) * K + kl + (int64_t)st * dp::KCH), w);
+      *reinterpret_cast<u32x4*>(base + sw256(16 * i + prow, pc)) = w;
+    }
 #pragma unroll
     for (int i = 0; i < RB; ++i) *reinterpret_cast<u32x4*>(base + dp::XB + sw256(16 * i + prow, pc)) = yr[i];
   };
@@ -109,12 +114,12 @@ __global__ __launch_bounds__(256) void down_proj_kernel(const uint16_t* __restri
   load(0, xa, ya);
   if (nst > 1) load(1, xb, yb);
   for (int st = 0; st < nst; st += 2) {
-    store(0, xa, ya);
+    store(0, st, xa, ya);
     if (st + 2 < nst) load(st + 2, xa, ya);
     __syncthreads();
     compute(0);
     if (st + 1 >= nst) break;
-    store(1, xb, yb);
+    store(1, st + 1, xb, yb);
     if (st + 3 < nst) load(st + 3, xb, yb);
     __syncthreads();
     compute(1);
@@ -149,12 +154,13 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ part, int 
   return s;
 }
 
-// out[i] = sum_s part[s][i] in split order (fp32)
+// out[i] = scale * sum_s part[s][i], summed in split order (fp32)
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t count,
-                                                            float* __restrict__ out) {
+                                                            float scale, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
-  out[i] = sum_splits(part, nsplit, count, i);
+  const float v = sum_splits(part, nsplit, count, i);
+  out[i] = scale == 1.0f ? v : scale * v;
 }
 
 // ---------------------------------------------------------------------------
@@ -185,7 +191,7 @@ __device__ __forceinline__ uint32_t swy(int q, int chunk) {
 template <int RB>
 __global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t J,
                                                          const float* __restrict__ Y, int R,
-                                                         float* __restrict__ part, int64_t tc) {
+                                                         float* __restrict__ part, int64_t tc, DropoutDev drop) {
   constexpr int PLANE = RB * 16 * 128;
   constexpr int STAGE = tg::XB + 2 * PLANE;
   __shared__ __align__(16) uint8_t lds[2 * STAGE];
@@ -239,9 +245,14 @@ __global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restr
   };
   auto store = [&](int buf, int st, const u32x4(&xr)[4], const u32x4(&yr)[RB]) {
     uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(base + swtg(16 * i + prow, pc)) = xr[i];
     const int64_t tb = tbeg + (int64_t)st * tg::TT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // dropout (adapter input only): X element (t, j) is e = t J + j
+      u32x4 w = xr[i];
+      if (drop.on) w = dropout8(drop, (uint64_t)((tb + 16 * i + prow) * J + j0 + 8 * pc), w);
+      *reinterpret_cast<u32x4*>(base + swtg(16 * i + prow, pc)) = w;
+    }
     const int tlim = (int)((tend - tb) < tg::TT ? (tend - tb) : tg::TT);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -617,19 +628,22 @@ int down_proj_splits(int64_t M, int64_t K, int R) {
   return (int)cdiv(K, cdiv(cdiv(K, want), dp::KCH) * dp::KCH);
 }
 
+// drop: dropout on X (the adapter input), or null; the result is scaled by
+// `scale` (1 / (1 - p) with dropout) after the fixed-order sum
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
-                      float* out, hipStream_t stream) {
+                      float* out, hipStream_t stream, const DropoutDev* drop, float scale) {
   const int64_t kc = cdiv(cdiv(K, splits), dp::KCH) * dp::KCH;
   const dim3 grid((unsigned)cdiv(M, dp::TT), (unsigned)splits);
+  const DropoutDev d = drop ? *drop : DropoutDev{0u, 0u, 0u, 0ull, 0};
   switch (rank_blocks(R)) {
-    case 1: hipLaunchKernelGGL(down_proj_kernel<1>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-    case 2: hipLaunchKernelGGL(down_proj_kernel<2>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-    case 4: hipLaunchKernelGGL(down_proj_kernel<4>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-    default: hipLaunchKernelGGL(down_proj_kernel<8>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+    case 1: hipLaunchKernelGGL(down_proj_kernel<1>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+    case 2: hipLaunchKernelGGL(down_proj_kernel<2>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+    case 4: hipLaunchKernelGGL(down_proj_kernel<4>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+    default: hipLaunchKernelGGL(down_proj_kernel<8>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
   }
   const int64_t count = M * R;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
-                     count, out);
+                     count, scale, out);
 }
 
 int token_grad_splits(int64_t M, int64_t J, int R) {
@@ -643,18 +657,82 @@ int token_grad_splits(int64_t M, int64_t J, int R) {
 }
 
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
-                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream) {
+                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
+                       const DropoutDev* drop) {
   const int64_t tc = cdiv(cdiv(M, splits), tg::TT) * tg::TT;
   const dim3 grid((unsigned)cdiv(J, tg::JT), (unsigned)splits);
+  const DropoutDev d = drop ? *drop : DropoutDev{0u, 0u, 0u, 0ull, 0};
   switch (rank_blocks(R)) {
-    case 1: hipLaunchKernelGGL(token_grad_kernel<1>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
-    case 2: hipLaunchKernelGGL(token_grad_kernel<2>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
-    case 4: hipLaunchKernelGGL(token_grad_kernel<4>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
-    default: hipLaunchKernelGGL(token_grad_kernel<8>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc); break;
+    case 1: hipLaunchKernelGGL(token_grad_kernel<1>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+    case 2: hipLaunchKernelGGL(token_grad_kernel<2>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+    case 4: hipLaunchKernelGGL(token_grad_kernel<4>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+    default: hipLaunchKernelGGL(token_grad_kernel<8>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
   }
   const int64_t count = Jout * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
                      Jout, R, s, transpose_out, out);
+}
+
+// The adapter part of grad_x under dropout, in fp32 for the grad_x GEMM to
+// add before its single bf16 rounding:
+//   out[t][f] = scale * keep(t, f) * sum_q v[t][q] A[q][f],  scale = s / (1 - p)
+// (the chain rule through the dropped adapter input).  Workgroup: 32 tokens x
+// 128 features; v rows and the A tile are staged in LDS; a thread owns 4
+// tokens x 4 consecutive features (one Philox call gives their 4 words).
+__global__ __launch_bounds__(256) void lora_dropout_term_kernel(const float* __restrict__ v,
+                                                                const uint16_t* __restrict__ A, int64_t M,
+                                                                int64_t n, int R, float scale, DropoutDev drop,
+                                                                float* __restrict__ out) {
+  __shared__ float sv[32][kMaxRank + 1];
+  __shared__ __align__(16) uint16_t sa[kMaxRank][128];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.y * 32;
+  const int64_t f0 = (int64_t)blockIdx.x * 128;
+  for (int i = tid; i < 32 * R; i += 256) {
+    const int t = i / R, q = i % R;
+    sv[t][q] = t0 + t < M ? v[(t0 + t) * R + q] : 0.0f;
+  }
+  for (int i = tid; i < R * 16; i += 256) {
+    const int q = i / 16, c = i % 16;
+    const int64_t f = f0 + 8 * c;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (f < n) w = *reinterpret_cast<const u32x4*>(A + (int64_t)q * n + f);
+    *reinterpret_cast<u32x4*>(&sa[q][8 * c]) = w;
+  }
+  __syncthreads();
+  const int fl = 4 * (tid & 31);
+  const int tl = 4 * (tid >> 5);
+  float acc[4][4] = {};
+  for (int q = 0; q < R; ++q) {
+    const uint32_t a01 = *reinterpret_cast<const uint32_t*>(&sa[q][fl]);
+    const uint32_t a23 = *reinterpret_cast<const uint32_t*>(&sa[q][fl + 2]);
+    const float a[4] = {bf16_lo_to_f32(a01), bf16_hi_to_f32(a01), bf16_lo_to_f32(a23), bf16_hi_to_f32(a23)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float vv = sv[tl + e][q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[e][c] = __builtin_fmaf(vv, a[c], acc[e][c]);
+    }
+  }
+  const int64_t f = f0 + fl;
+  if (f >= n) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t t = t0 + tl + e;
+    if (t >= M) break;
+    const uint64_t c = ((uint64_t)(t * n + f) >> 2) + drop.offset;
+    const u32x4 r = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), drop.k0, drop.k1);
+    f32x4 o;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) o[cc] = r[cc] >= drop.thr ? scale * acc[e][cc] : 0.0f;
+    *reinterpret_cast<f32x4*>(out + t * n + f) = o;
+  }
+}
+
+void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
+                              const DropoutDev& drop, float* out, hipStream_t stream) {
+  const dim3 grid((unsigned)cdiv(n, 128), (unsigned)cdiv(M, 32));
+  hipLaunchKernelGGL(lora_dropout_term_kernel, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out);
 }
 
 // v and grad_B from one read of g (R % 8 == 0, R <= 32): vpart holds
@@ -674,7 +752,7 @@ void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, in
     hipLaunchKernelGGL((gpass_kernel<2, 2>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
   const int64_t count = M * R;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
-                     v);
+                     1.0f, v);
   const int64_t gcount = m * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(gcount, 256)), dim3(256), 0, stream, gbpart, st, J, m,
                      R, s, 0, grad_B);

@@ -122,6 +122,53 @@ __device__ __forceinline__ void mag_dequant8(const MagLut& L, uint32_t w, uint32
 }
 
 
+// LoRA dropout on the adapter input ("QLoRA: Efficient Fine-Tuning", the
+// LoraConfig snippet's lora_dropout).  Element e of a row-major tensor takes
+// word e % 4 of Philox4x32-10 at the 64-bit counter e / 4 + offset (upper two
+// counter words zero) under the key (seed low, seed high), and is kept when
+// that word is at least thr = round(p 2^32).  Philox4x32-10 as defined by
+// Salmon, Moraes, Dror and Shaw (SC 2011): per round the counter words 0 and
+// 2 are multiplied by two constants and the halves mixed with the key, which
+// takes two Weyl increments between rounds.
+struct DropoutDev {
+  uint32_t thr;       // 0: keep everything
+  uint32_t k0, k1;    // key (seed)
+  uint64_t offset;    // counter offset
+  int on;             // apply the mask at all
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// 8 consecutive bf16 elements e0 .. e0 + 7 (e0 % 4 == 0, two bf16 per word,
+// element order) with the dropped ones set to zero.
+__device__ __forceinline__ u32x4 dropout8(const DropoutDev& d, uint64_t e0, u32x4 w) {
+  const uint64_t c = (e0 >> 2) + d.offset;
+  const u32x4 r0 = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), d.k0, d.k1);
+  const uint64_t c1 = c + 1;
+  const u32x4 r1 = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), d.k0, d.k1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = (j < 2 ? r0[2 * j] : r1[2 * j - 4]) >= d.thr ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (j < 2 ? r0[2 * j + 1] : r1[2 * j - 3]) >= d.thr ? 0xFFFF0000u : 0u;
+    w[j] &= lo | hi;
+  }
+  return w;
+}
+
 // Raw buffer access with a byte range: lanes whose offset is past `bytes`
 // read 0 instead of touching memory.  All offsets go in the per-lane VGPR
 // offset (the range check covers it).

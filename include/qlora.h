@@ -190,11 +190,14 @@ qlora_status qlora_dequant_dq(int32_t qtype, const uint8_t* codes, const uint8_t
 /* Operation ids for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1
+#define QLORA_OP_BWD_DROPOUT 2 /* qlora_linear_bwd_ex with dropout on */
 
 /*
- * Workspace bytes needed by qlora_linear_fwd (op 0) or qlora_linear_bwd
- * (op 1) for these sizes; 0 on invalid arguments.  The bwd figure assumes u
- * is recomputed (the most it can need).
+ * Workspace bytes needed by qlora_linear_fwd (op 0, also
+ * qlora_linear_fwd_ex), qlora_linear_bwd (op 1, also qlora_linear_bwd_ex
+ * without dropout) or qlora_linear_bwd_ex with dropout (op 2: an M x n fp32
+ * buffer more) for these sizes; 0 on invalid arguments.  The bwd figures
+ * assume u is recomputed (the most they can need).
  */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t n, int64_t m, int32_t r);
 
@@ -279,12 +282,66 @@ qlora_status qlora_linear_bwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
                               qlora_stream_t stream);
 
 /*
+ * LoRA dropout on the adapter input ("QLoRA: Efficient Fine-Tuning", the
+ * LoraConfig snippet's lora_dropout, with Step 3's adapter branch): the
+ * adapter reads x_d = x * keep / (1 - p) instead of x, while the frozen
+ * weight still reads x.  Host struct.
+ *   p       drop probability, 0 <= p < 1 (p = 0 is the plain layer).
+ *   seed    Philox key: low and high 32-bit words.
+ *   offset  added to every counter (advance it by ceil(M n / 4) per call
+ *           for a fresh mask).
+ * Mask: element e = t n + k of x takes word e % 4 of Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, SC 2011) at the 64-bit counter e / 4 + offset (low
+ * word first, upper two words zero), and is kept when that word is at least
+ * round(p 2^32) (ties to even, capped at 2^32 - 1).  The forward and the
+ * backward with the same struct draw the same mask.
+ */
+typedef struct {
+  float p;
+  uint64_t seed;
+  uint64_t offset;
+} qlora_dropout;
+
+/*
+ * qlora_linear_fwd with dropout on the adapter input (NULL or p = 0: exactly
+ * qlora_linear_fwd):
+ *   u = (x * keep) A^T / (1 - p),   h = bf16(x W'^T + s u B^T)
+ * u_out receives that u (the backward's grad_B needs it).  Workspace as for
+ * qlora_linear_fwd.  QLORA_ERR_VALUE when p is outside [0, 1) or not finite.
+ */
+qlora_status qlora_linear_fwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                 const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                 const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
+                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
+                                 qlora_stream_t stream);
+
+/*
+ * qlora_linear_bwd for the forward above, with the same mask (NULL or
+ * p = 0: exactly qlora_linear_bwd).  Chain rule with the mask fixed:
+ *   v      = g B
+ *   grad_x = bf16(g W' + s (v A) * keep / (1 - p))
+ *   grad_A = bf16(s v^T (x * keep) / (1 - p))
+ *   grad_B = bf16(s g^T u)
+ * u: the forward's u_out (with the mask), or NULL to recompute it with the
+ * mask.  The adapter part of grad_x is formed in fp32 (an M x n buffer in
+ * the workspace) and added before the single rounding.  Workspace: at least
+ * qlora_workspace_bytes(QLORA_OP_BWD_DROPOUT, ...) when p > 0.
+ */
+qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                 const qlora_bf16* g, const uint8_t* codes, const uint8_t* absmax8,
+                                 const float* c2, const qlora_bf16* A, const qlora_bf16* B, const float* u,
+                                 qlora_bf16* grad_x, qlora_bf16* grad_A, qlora_bf16* grad_B,
+                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
+                                 qlora_stream_t stream);
+
+/*
  * Kernel timing (tracing aid, off by default).  While enabled, every kernel
  * the library launches is bracketed by HIP events on its stream.
  * qlora_profile_enable(1) clears earlier records; (0) stops recording.
  * qlora_profile_query waits for the recorded events of kernel `name`
  * ("quantize", "dequant", "fwd_gemm", "fwd_small", "dgrad_gemm",
- * "down_proj", "token_grad", "transpose") and reports the launch
+ * "down_proj", "token_grad", "transpose", "gpass", "dropout_term", "merge",
+ * "adam") and reports the launch
  * count and the summed duration in milliseconds (host pointers).
  */
 qlora_status qlora_profile_enable(int on);

@@ -496,6 +496,51 @@ def dropout_mask(M: int, n: int, p: float, seed: int, offset: int = 0) -> np.nda
     return (words[:total] >= thr).reshape(M, n)
 
 
+def philox4x32_10_np(ctr_lo, ctr_hi, key):
+    """philox4x32_10 over arrays of counters (words 2 and 3 zero), the same
+    rounds in numpy uint64 arithmetic (each 32 x 32-bit product fits).
+    Returns the four output words as uint64 arrays."""
+    m32 = np.uint64(0xFFFFFFFF)
+    c0 = np.asarray(ctr_lo, dtype=np.uint64) & m32
+    c1 = np.asarray(ctr_hi, dtype=np.uint64) & m32
+    c2 = np.zeros_like(c0)
+    c3 = np.zeros_like(c0)
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    for r in range(10):
+        if r:
+            k0 = (k0 + PHILOX_W0) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W1) & 0xFFFFFFFF
+        p0 = np.uint64(PHILOX_M0) * c0
+        p1 = np.uint64(PHILOX_M1) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ np.uint64(k0), p1 & m32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ np.uint64(k1), p0 & m32)
+    return c0, c1, c2, c3
+
+
+def dropout_mask_np(M: int, n: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """dropout_mask vectorized over the counters (for large tensors)."""
+    total = M * n
+    nctr = (total + 3) // 4
+    ctr = np.arange(nctr, dtype=np.uint64) + np.uint64(offset)   # wraps like the 64-bit counter
+    words = philox4x32_10_np(ctr & np.uint64(0xFFFFFFFF), ctr >> np.uint64(32),
+                             (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    w = np.stack(words, axis=1).reshape(-1)[:total]
+    return (w >= np.uint64(dropout_keep_threshold(p))).reshape(M, n)
+
+
+def dropout_mask_at(rows, cols, n: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """dropout_mask restricted to the elements (rows x cols) of an (any) x n
+    tensor, vectorized: for sampled outputs of large tensors."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    cols = np.asarray(cols, dtype=np.uint64)
+    e = rows[:, None] * np.uint64(n) + cols[None, :]
+    ctr = (e >> np.uint64(2)) + np.uint64(offset)   # offsets near 2^64 wrap like the 64-bit counter
+    words = philox4x32_10_np(ctr & np.uint64(0xFFFFFFFF), ctr >> np.uint64(32),
+                             (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    w = np.select([(e & np.uint64(3)) == np.uint64(j) for j in range(4)], list(words))
+    return w >= np.uint64(dropout_keep_threshold(p))
+
+
 def linear_fwd_dropout(x, Wd, A, B, s: float, keep, p: float):
     """Forward with dropout on the adapter input: u = (x * keep / (1 - p)) A^T,
     h = x W'^T + s u B^T.  [P1] Step 3, Eq. 3 and the snippet's lora_dropout."""

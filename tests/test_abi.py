@@ -177,3 +177,32 @@ def test_grouped_argument_errors(lib):
     # the grouped workspace is the sum of the single-layer ones, each rounded to 256 bytes
     singles = [lib.qlora_workspace_bytes(0, 16, d.n, d.m, d.r) for d in arr]
     assert need == sum((b + 255) // 256 * 256 for b in singles)
+
+
+def test_dropout_argument_errors(lib):
+    from bit_quantized_fine_qlora_amd import _lib
+    fwd_ex, bwd_ex = lib.qlora_linear_fwd_ex, lib.qlora_linear_bwd_ex
+
+    def drop(p):
+        return ctypes.pointer(_lib.Dropout(p, 7, 0))
+
+    def f(d, x=P):
+        return fwd_ex(32, 256, 256, 8, 2.0, x, P, P, P, P, P, P, None, d, P, 1 << 30, None)
+
+    def b(d, ws=P, wsb=1 << 30, gA=P):
+        return bwd_ex(32, 256, 256, 8, 2.0, P, P, P, P, P, P, P, None, P, gA, P, d, ws, wsb, None)
+
+    for p in (-0.25, 1.0, 1.5, float("nan"), float("inf")):
+        assert f(drop(p)) == -7, p
+        assert b(drop(p)) == -7, p
+    assert f(None, x=None) == -1
+    assert f(drop(0.1), x=None) == -1
+    assert b(drop(0.1), gA=None) == -1
+    # with the mask on, the backward needs the dropout workspace (one M x n
+    # fp32 buffer more than the plain backward)
+    plain = lib.qlora_workspace_bytes(1, 32, 256, 256, 8)
+    need = lib.qlora_workspace_bytes(2, 32, 256, 256, 8)
+    assert need == plain + 32 * 256 * 4
+    assert b(drop(0.1), wsb=plain) == -5
+    assert b(drop(0.1), wsb=need - 1) == -5
+    assert b(drop(0.1), ws=None, wsb=need) == -5

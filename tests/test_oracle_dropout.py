@@ -80,3 +80,25 @@ def test_backward_matches_autograd_with_fixed_mask():
     assert np.allclose(bw["grad_B"], tB.grad.numpy(), rtol=1e-12, atol=1e-12)
     hf, _ = O.linear_fwd_dropout(x, Wd, A, B, s, keep, p)
     assert np.allclose(hf, h.detach().numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_vectorized_mask_matches_the_scalar_generator():
+    # the array form of the generator against the scalar one (itself pinned by
+    # the known answers): every word of random counters, and whole masks,
+    # including a counter offset that carries into the high word
+    rng = np.random.default_rng(9)
+    ctrs = [int(c) for c in rng.integers(0, 2 ** 63, 40)] + [0xFFFFFFFF, 0x100000000, 2 ** 64 - 1]
+    key = (0x9ABCDEF0, 0x12345678)
+    lo = np.array([c & 0xFFFFFFFF for c in ctrs], dtype=np.uint64)
+    hi = np.array([c >> 32 for c in ctrs], dtype=np.uint64)
+    got = O.philox4x32_10_np(lo, hi, key)
+    for i, c in enumerate(ctrs):
+        want = O.philox4x32_10((c & 0xFFFFFFFF, c >> 32, 0, 0), key)
+        assert [int(w[i]) for w in got] == want, hex(c)
+    for (M, n, p, seed, off) in ((5, 64, 0.3, 77, 0), (3, 128, 0.05, 2 ** 40 + 3, 2 ** 32 - 20)):
+        full = O.dropout_mask(M, n, p, seed, off)
+        sub = O.dropout_mask_at(np.arange(M), np.arange(n), n, p, seed, off)
+        assert np.array_equal(full, sub)
+        assert np.array_equal(full, O.dropout_mask_np(M, n, p, seed, off))
+        rows, cols = np.array([4 % M, 0]), np.array([63, 1, 8])
+        assert np.array_equal(O.dropout_mask_at(rows, cols, n, p, seed, off), full[np.ix_(rows, cols)])
