@@ -253,6 +253,39 @@ def adapter_adam(Q, dev, reps):
     return out
 
 
+def dropout_passes(Q, x, g, q, A, B, s, h, u, out, ws_f, plain, reps):
+    """Forward and backward with dropout p = 0.05 on the adapter input, against
+    the plain passes; the fp32 adapter term of grad_x as its own kernel."""
+    import torch
+    M, n = x.shape
+    m, r = q.m, A.shape[0]
+    drop = (0.05, 1234, 0)
+    ws_bd = torch.empty(Q.workspace_bytes(Q.QLORA_OP_BWD_DROPOUT, M, n, m, r), dtype=torch.uint8, device=x.device)
+    fwd = lambda: Q.linear_fwd(x, q, A, B, s, h=h, u=u, workspace=ws_f, dropout=drop)  # noqa: E731
+    bwd = lambda: Q.linear_bwd(x, g, q, A, B, s, u=u, out=out, workspace=ws_bd, dropout=drop)  # noqa: E731
+    fwd_med, _ = timed_us(fwd, reps)
+    bwd_med, _ = timed_us(bwd, reps)
+    Q.profile_enable(True)
+    for _ in range(reps):
+        bwd()
+    torch.cuda.synchronize()
+    Q.profile_enable(False)
+    kern = {}
+    for name in ("dropout_term", "dgrad_gemm", "down_proj", "token_grad", "gpass"):
+        cnt, tot = Q.profile_query(name)
+        if cnt:
+            kern[name] = round(tot * 1e3 / cnt, 2)
+    # dropout term: v (M r fp32) and A (r n bf16) read, M n fp32 written
+    tb = M * r * 4 + r * n * 2 + M * n * 4
+    du = kern.get("dropout_term", 0.0)
+    return {"workload": f"gate projection {m}x{n}, {M} tokens, r={r}, p=0.05",
+            "forward_us": round(fwd_med, 2), "backward_us": round(bwd_med, 2),
+            "forward_vs_plain": round(fwd_med / plain["forward"]["us"], 3),
+            "backward_vs_plain": round(bwd_med / plain["backward"]["us"], 3),
+            "kernels_us": kern,
+            "dropout_term": {"bytes": tb, "GB/s": round(tb / (du * 1e-6) / 1e9, 1) if du else None}}
+
+
 def cpu_baseline(cfg, layer, tokens):
     """Time the oracle (float64 numpy) on a bounded sample of the workload."""
     import numpy as np
@@ -417,6 +450,7 @@ def main():
     }
     out.update(extra)
     if not args.no_extra:
+        out["dropout"] = dropout_passes(Q, x, g, q, A, B, s, h, u, (gx, gA, gB), ws_f, extra["passes"], 10)
         out["adapter_merge"] = adapter_merge(Q, q, A, B, s, 10)
         out["adapter_adam"] = adapter_adam(Q, dev, 10)
         out["level_tables"] = level_table_variants(Q, W, q, 10)

@@ -679,12 +679,15 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
 // (the chain rule through the dropped adapter input).  Workgroup: 32 tokens x
 // 128 features; v rows and the A tile are staged in LDS; a thread owns 4
 // tokens x 4 consecutive features (one Philox call gives their 4 words).
+// LDS is sized to the rank (RB blocks of 16), so small ranks keep many
+// workgroups per CU.
+template <int RB>
 __global__ __launch_bounds__(256) void lora_dropout_term_kernel(const float* __restrict__ v,
                                                                 const uint16_t* __restrict__ A, int64_t M,
                                                                 int64_t n, int R, float scale, DropoutDev drop,
                                                                 float* __restrict__ out) {
-  __shared__ float sv[32][kMaxRank + 1];
-  __shared__ __align__(16) uint16_t sa[kMaxRank][128];
+  __shared__ float sv[32][16 * RB + 1];
+  __shared__ __align__(16) uint16_t sa[16 * RB][128];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.y * 32;
   const int64_t f0 = (int64_t)blockIdx.x * 128;
@@ -732,7 +735,12 @@ __global__ __launch_bounds__(256) void lora_dropout_term_kernel(const float* __r
 void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
                               const DropoutDev& drop, float* out, hipStream_t stream) {
   const dim3 grid((unsigned)cdiv(n, 128), (unsigned)cdiv(M, 32));
-  hipLaunchKernelGGL(lora_dropout_term_kernel, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out);
+  switch (rank_blocks(R)) {
+    case 1: hipLaunchKernelGGL(lora_dropout_term_kernel<1>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
+    case 2: hipLaunchKernelGGL(lora_dropout_term_kernel<2>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
+    case 4: hipLaunchKernelGGL(lora_dropout_term_kernel<4>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
+    default: hipLaunchKernelGGL(lora_dropout_term_kernel<8>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
+  }
 }
 
 // v and grad_B from one read of g (R % 8 == 0, R <= 32): vpart holds
