@@ -44,19 +44,21 @@ constexpr int BK = 64;               // K per step
 // a ds_read_b128 serves 16 lanes, conflict-free when bits 4-7 differ; a
 // ds_read_b64_tr_b16 serves 16 lanes (4 rows x 32 bytes), conflict-free when
 // the four 32-byte runs do not overlap modulo 256 bytes.
-//   forward W' [256 rows][64 K] bf16: pitch 144 = 9 x 16, so 8 or 16
-//     consecutive rows at one chunk fall on distinct slots.
 //   activations [256 rows][64 K] bf16: pitch 128, written 1 KB (8 rows) at a
 //     time by the direct-to-LDS loads, so the 16-byte chunk c of row r sits
 //     at position c ^ (r & 7) instead (the loads pick their sources to match).
+//   forward W' [256 rows][64 K] bf16: the same layout as the activations
+//     (its fragment reads have the same shape).  A pitch of 144 bytes, which
+//     puts 16 consecutive rows on distinct 16-byte slots, measured 2-way
+//     conflicted on these reads (the bank-conflict counter and the time of
+//     a read-only loop both doubled), while the XOR layout reads free.
 //   backward W' [64 K rows][256 features]: pitch 560 = 35 x 16; a dequant
 //     store (8 consecutive rows, one chunk) hits slots 3r + d mod 8, and the
 //     4 consecutive rows of a transposed read start 48 bytes apart.
-constexpr int AP = 144;
 constexpr int WPB = 560;
 constexpr int ATILEB = BT * 128;     // 32 KB
 template <bool kBwd> struct Tile {
-  static constexpr int W = kBwd ? BK * WPB : BF * AP;  // 35 / 36 KB
+  static constexpr int W = kBwd ? BK * WPB : BF * 128;  // 35 / 32 KB
 };
 // The four LDS tiles are separate arrays (136 KB in all): the compiler then
 // knows that reading one stage does not alias the direct-to-LDS copy into
@@ -154,7 +156,10 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
     float sa;       // c2 of the group
   };
   using T = lg2::Tile<kBwd>;
-  const uint32_t w_st = kBwd ? (uint32_t)((pt & 63) * lg2::WPB + 128 * (pt >> 6)) : (uint32_t)(pt * lg2::AP);
+  const uint32_t w_st = kBwd ? (uint32_t)((pt & 63) * lg2::WPB + 128 * (pt >> 6)) : (uint32_t)(pt * 128);
+  // byte offset of 16-byte chunk d of this thread's W' piece (forward: XOR
+  // layout of row pt, see the pitch notes)
+  auto wchunk = [&](int d) -> uint32_t { return kBwd ? (uint32_t)(16 * d) : (uint32_t)((d ^ (pt & 7)) << 4); };
   auto load = [&](Regs& R) {
     R.code[0] = bload128(r_codes, c_off);
     R.code[1] = bload128(r_codes, c_off + 16);
@@ -170,7 +175,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
     for (int d = 0; d < 8; ++d) {
       uint32_t o[4];
       mag_dequant8(L, R.code[d >> 2][d & 3], o);
-      *reinterpret_cast<u32x4*>(dW + 16 * d) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4*>(dW + wchunk(d)) = u32x4{o[0], o[1], o[2], o[3]};
     }
   };
   // K step ks: `cur` holds step ks + 1, `nxt` receives step ks + 2.  The
@@ -243,7 +248,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const u32x4 v = kBwd ? LR.f[d] : LR.f[d & 3];
-      *reinterpret_cast<u32x4*>(wtile + w_st + 16 * d) = v;
+      *reinterpret_cast<u32x4*>(wtile + w_st + wchunk(d)) = v;
     }
     // activation row pt: chunk c at position c ^ (pt % 8)
     uint8_t* arow = atile + pt * 128;
@@ -339,11 +344,12 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   const uint32_t a_base0 = (uint32_t)((wt + lr) * 128 + ((lq ^ (lr & 7)) << 4));
   const uint32_t a_base1 = a_base0 ^ 64u;
   const uint32_t w_base = kBwd ? (uint32_t)((8 * lq + (lr >> 2)) * lg2::WPB + 2 * (wf + 4 * (lr & 3)))
-                               : (uint32_t)((wf + lr) * lg2::AP + 16 * lq);
+                               : (uint32_t)((wf + lr) * 128 + ((lq ^ (lr & 7)) << 4));
   // A fragment i of step kk
   auto load_a = [&](const uint8_t* sW, int kk, int i) -> u32x4 {
     if (!kBwd) {
-      return *reinterpret_cast<const u32x4*>(sW + w_base + 64 * kk + 16 * lg2::AP * i);
+      // chunk 4 kk + lq of row wf + 16 i + lr: position (4 kk + lq) ^ (lr % 8)
+      return *reinterpret_cast<const u32x4*>(sW + (kk ? (w_base ^ 64u) : w_base) + 2048 * i);
     } else {
       const uint8_t* src = sW + w_base + 32 * lg2::WPB * kk + 32 * i;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
