@@ -25,10 +25,11 @@
 // the MFMA waves also start the copy of the next activation tile (256 x 64)
 // with buffer loads that write LDS directly (no registers, 4 per wave).  The forward reads W' with
 // ds_read_b128; the backward contracts over W0's rows, so it reads the
-// natural-layout tile transposed with ds_read_b64_tr_b16.  LDS rows are
-// padded (pitches below) so that every store and fragment read is free of
-// bank conflicts and every fragment address is one per-lane base plus an
-// immediate offset.  Two LDS stages of {W', activations}: 134-136 KB.  The
+// natural-layout tile transposed with ds_read_b64_tr_b16.  The LDS layouts
+// below keep every store and the forward's fragment reads free of bank
+// conflicts, and every fragment address is one per-lane base plus an
+// immediate offset.  Two LDS stages of {W', activations}: 128 KB forward,
+// 134 KB backward.  The
 // LoRA term runs as extra K steps whose tiles the producers fill from the
 // adapter factors.
 #include "qlora_common.h"
@@ -39,11 +40,8 @@ namespace lg2 {
 constexpr int BF = 256;              // output features per tile
 constexpr int BT = 256;              // tokens per tile
 constexpr int BK = 64;               // K per step
-// LDS row pitches.  Measured bank rules: a ds_write_b128 serves 8 lanes per
-// cycle, conflict-free when their 16-byte slots differ in address bits 4-6;
-// a ds_read_b128 serves 16 lanes, conflict-free when bits 4-7 differ; a
-// ds_read_b64_tr_b16 serves 16 lanes (4 rows x 32 bytes), conflict-free when
-// the four 32-byte runs do not overlap modulo 256 bytes.
+// LDS layouts, checked with the bank-conflict counter on loops of each
+// access stream (LDS: 256 bytes per cycle).
 //   activations [256 rows][64 K] bf16: pitch 128, written 1 KB (8 rows) at a
 //     time by the direct-to-LDS loads, so the 16-byte chunk c of row r sits
 //     at position c ^ (r & 7) instead (the loads pick their sources to match).
@@ -52,9 +50,13 @@ constexpr int BK = 64;               // K per step
 //     puts 16 consecutive rows on distinct 16-byte slots, measured 2-way
 //     conflicted on these reads (the bank-conflict counter and the time of
 //     a read-only loop both doubled), while the XOR layout reads free.
-//   backward W' [64 K rows][256 features]: pitch 560 = 35 x 16; a dequant
-//     store (8 consecutive rows, one chunk) hits slots 3r + d mod 8, and the
-//     4 consecutive rows of a transposed read start 48 bytes apart.
+//   backward W' [64 K rows][256 features]: pitch 560 = 35 x 16; dequant
+//     stores are conflict-free.  A ds_read_b64_tr_b16 serves 32 lanes (8 rows
+//     x 32 bytes) per cycle, and rows r and r + 8 of one cycle overlap here,
+//     so the transposed reads take 1.5x their conflict-free LDS cycles.  A
+//     pitch-512 layout with a row-dependent chunk XOR removes that, but its
+//     per-read address XORs in the MFMA waves cost as much as it saved (the
+//     grad_x GEMM time did not change), so this layout stays.
 constexpr int WPB = 560;
 constexpr int ATILEB = BT * 128;     // 32 KB
 template <bool kBwd> struct Tile {
@@ -157,9 +159,17 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
   };
   using T = lg2::Tile<kBwd>;
   const uint32_t w_st = kBwd ? (uint32_t)((pt & 63) * lg2::WPB + 128 * (pt >> 6)) : (uint32_t)(pt * 128);
-  // byte offset of 16-byte chunk d of this thread's W' piece (forward: XOR
-  // layout of row pt, see the pitch notes)
-  auto wchunk = [&](int d) -> uint32_t { return kBwd ? (uint32_t)(16 * d) : (uint32_t)((d ^ (pt & 7)) << 4); };
+  // Address of 16-byte chunk d of this thread's W' piece.  Forward: row pt
+  // in the XOR layout, i.e. w_row ^ 16 d with w_row = 128 pt + 16 (pt % 8)
+  // (d flips only address bits 4-6); the base is made opaque at each store
+  // so the eight addresses cost one XOR each instead of eight registers.
+  const uint32_t w_row = kBwd ? w_st : (uint32_t)(pt * 128 + ((pt & 7) << 4));
+  auto wbase = [&]() -> uint32_t {
+    uint32_t b = w_row;
+    if (!kBwd) asm volatile("" : "+v"(b));
+    return b;
+  };
+  auto wchunk = [&](uint32_t b, int d) -> uint32_t { return kBwd ? b + (uint32_t)(16 * d) : b ^ (uint32_t)(16 * d); };
   auto load = [&](Regs& R) {
     R.code[0] = bload128(r_codes, c_off);
     R.code[1] = bload128(r_codes, c_off + 16);
@@ -169,13 +179,13 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
     b_off += b_step;
   };
   auto store = [&](const Regs& R, uint8_t* tile) {
-    uint8_t* dW = tile + w_st;
+    const uint32_t wb = wbase();
     const MagLut L = make_mag_lut(tab, e4m3_decode((uint32_t)R.aa) * R.sa);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       uint32_t o[4];
       mag_dequant8(L, R.code[d >> 2][d & 3], o);
-      *reinterpret_cast<u32x4*>(dW + wchunk(d)) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4*>(tile + wchunk(wb, d)) = u32x4{o[0], o[1], o[2], o[3]};
     }
   };
   // K step ks: `cur` holds step ks + 1, `nxt` receives step ks + 2.  The
@@ -248,7 +258,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const u32x4 v = kBwd ? LR.f[d] : LR.f[d & 3];
-      *reinterpret_cast<u32x4*>(wtile + w_st + wchunk(d)) = v;
+      *reinterpret_cast<u32x4*>(wtile + wchunk(wbase(), d)) = v;
     }
     // activation row pt: chunk c at position c ^ (pt % 8)
     uint8_t* arow = atile + pt * 128;
