@@ -122,7 +122,7 @@ def small_token_block(Q, dev, reps):
     import torch
 
     import qlora_inputs as QI
-    cfg = QI.CONFIGS[4]
+    cfg = QI.WORKLOADS[4]
     gen = torch.Generator(device=dev).manual_seed(4)
     Ws, layers = [], []
     for L in cfg["layers"]:
@@ -204,7 +204,7 @@ def adapter_adam(Q, dev, reps):
     import torch
 
     import qlora_inputs as QI
-    layers = QI.CONFIGS[4]["layers"]
+    layers = QI.WORKLOADS[4]["layers"]
     shapes = []
     for _ in range(32):
         for L in layers:
@@ -358,7 +358,7 @@ def main():
         return
 
     cfg = 2
-    L = QI.CONFIGS[cfg]["layers"][0]
+    L = QI.WORKLOADS[cfg]["layers"][0]
     M, n, m, r, s = L.M, L.n, L.m, L.r, L.s
     inp = QI.layer_inputs(cfg, L)
 

@@ -52,7 +52,7 @@ def _block(hidden, kv, ffn, M, r, alpha, sigma):
 # tokens, 3 the 8B down projection at 4096 tokens with r = 64, 4 the seven
 # layers of an 8B block at 16 tokens (forward only), 5 the seven layers of a
 # 70B block at 8192 tokens.
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="single 256x256 layer, 32 tokens, r=8",
             layers=[Layer("single", 256, 256, 32, 8, 16.0, 0.02, 0)], backward=True),
     2: dict(name="8B gate projection 14336x4096, 4096 tokens, r=16",

@@ -164,7 +164,7 @@ def test_mask_exact_on_grad_A(Q):
 
 def test_full_size_layer_sampled(Q):
     # the 14336 x 4096 gate projection, 4096 tokens, rank 16, p = 0.05
-    L = QI.CONFIGS[2]["layers"][0]
+    L = QI.WORKLOADS[2]["layers"][0]
     p, seed, offset = f32(0.05), 2024, 77
     say(f"dropout full size {L.name} {L.m}x{L.n} M={L.M} r={L.r}: drawing inputs")
     inp = QI.layer_inputs(2, L)

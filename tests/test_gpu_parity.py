@@ -71,7 +71,7 @@ def check_full(Q, W, inp, s, need_bwd=True, label=""):
 # ------------------------------------------------------------------ small
 
 def test_config1_full(Q):
-    L = QI.CONFIGS[1]["layers"][0]
+    L = QI.WORKLOADS[1]["layers"][0]
     inp = QI.layer_inputs(1, L)
     got, ref = check_full(Q, inp["W"], inp, L.s, label="config1")
     # u recomputed inside the backward gives the same bits
@@ -190,7 +190,7 @@ def test_grouped_forward_large_tokens(Q):
 
 def test_grouped_full_block_matches_single_layers(Q):
     # the seven layers of the 8B-shaped block at 16 tokens, in one grouped call
-    cfg = QI.CONFIGS[4]
+    cfg = QI.WORKLOADS[4]
     gen = torch.Generator(device="cuda").manual_seed(4)
     layers = []
     for L in cfg["layers"]:
@@ -384,7 +384,7 @@ def test_merge_adapter(Q, m, n, r, s):
 
 def test_merge_adapter_full_size_gate(Q):
     # the gate projection of the 8B-shaped block (14336 x 4096, r = 16), rows sampled
-    L = QI.CONFIGS[2]["layers"][0]
+    L = QI.WORKLOADS[2]["layers"][0]
     inp = QI.layer_inputs(2, L, tensors=("W", "A", "B"))
     say(f"merge full size {L.m}x{L.n}: oracle quantize")
     qw = O.quantize_nf4_dq(inp["W"])
@@ -453,11 +453,11 @@ def full_layer_case(Q, cfg, layer, need_bwd):
     assert_close(f64(host_bits(got["grad_B"][rc])), gB_ref, f"config{cfg} {L.name} grad_B (sampled)")
 
 
-FULL = [(2, L) for L in QI.CONFIGS[2]["layers"]] + [(3, L) for L in QI.CONFIGS[3]["layers"]] \
-    + [(4, L) for L in QI.CONFIGS[4]["layers"]] + [(5, L) for L in QI.CONFIGS[5]["layers"]]
+FULL = [(2, L) for L in QI.WORKLOADS[2]["layers"]] + [(3, L) for L in QI.WORKLOADS[3]["layers"]] \
+    + [(4, L) for L in QI.WORKLOADS[4]["layers"]] + [(5, L) for L in QI.WORKLOADS[5]["layers"]]
 
 
 @pytest.mark.parametrize("cfg,layer", FULL, ids=[f"cfg{c}-{L.name}" for c, L in FULL])
 def test_full_size_layer(Q, cfg, layer):
-    full_layer_case(Q, cfg, layer, need_bwd=QI.CONFIGS[cfg]["backward"])
+    full_layer_case(Q, cfg, layer, need_bwd=QI.WORKLOADS[cfg]["backward"])
     torch.cuda.empty_cache()

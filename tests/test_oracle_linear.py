@@ -113,7 +113,7 @@ def test_b_zero_gives_zero_grad_a():
 
 def test_loops_match_vectorized_on_config1_shapes():
     # the real config-1 inputs, a slice of tokens to keep the loops short
-    L = QI.CONFIGS[1]["layers"][0]
+    L = QI.WORKLOADS[1]["layers"][0]
     inp = QI.layer_inputs(1, L, M=4)
     qw = O.quantize_nf4_dq(inp["W"])
     Wd = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], L.m * L.n)).reshape(L.m, L.n)

@@ -207,7 +207,7 @@ def test_worked_example_8b_and_70b(pages):
 
 
 def test_adapter_counts_pin_the_8b_block_shapes(pages):
-    layers = QI.CONFIGS[4]["layers"]
+    layers = QI.WORKLOADS[4]["layers"]
     per_block = sum(O.adapter_params(L.m, L.n, 16) for L in layers)
     assert per_block == pages["llama31_8b_adapter_params_per_block_r16"]["value"]
     total = per_block * pages["llama31_8b_adapter_params_total_r16"]["layers"]
