@@ -38,6 +38,8 @@ constexpr int kPW = (KC / 4) / PIECE;   // pieces per wave and feature block (2)
 constexpr int kDepth = 2;    // code pieces in flight per wave (deeper queues only delay x)
 constexpr int kMaxLayers = 8;
 constexpr int kTargetWGs = 512;         // two workgroups per CU
+constexpr int XCPR = KC / 4 / 8;         // 16-byte chunks of one token row of a wave's x quarter
+constexpr int XRPL = 64 / XCPR;          // token rows per 64-lane load of the x quarter
 }  // namespace sm
 
 // feature blocks (of 16) per workgroup at most: 16 for up to 16 tokens, 8 for 17..32
@@ -88,9 +90,9 @@ __device__ __forceinline__ int find_layer(const SmallArgs& a, int64_t key, int w
   return li;
 }
 
-// A wave's x quarter in LDS: token row t holds 512 bf16 (64 chunks of 16 B);
-// chunk c of row t sits at position c ^ (t & 15), so the 16 tokens of one
-// MFMA B fragment hit 16 different bank groups.
+// A wave's x quarter in LDS: token row t holds KC / 4 bf16 (XCPR chunks of
+// 16 B); chunk c of row t sits at position c ^ (t & 15), so the 16 tokens of
+// one MFMA B fragment hit 16 different bank groups.
 __device__ __forceinline__ uint32_t xsw(int t, int c) {
   return (uint32_t)(t * (sm::KC / 4 * 2) + ((c ^ (t & 15)) << 4));
 }
@@ -120,12 +122,14 @@ __device__ void small_u_chunk(const SmallArgs& a, uint8_t* lds, f32x4* ured) {
   const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
   const brsrc_t rx = make_rsrc(Ly.x, xbytes);
 #pragma unroll
-  for (int t = 0; t < MP; ++t) {
-    const int64_t k = k0 + kq + 8 * lane;
+  for (int i = 0; i < MP / sm::XRPL; ++i) {
+    const int t = sm::XRPL * i + lane / sm::XCPR;
+    const int c = lane % sm::XCPR;
+    const int64_t k = k0 + kq + 8 * c;
     const bool ok = t < M && k < K;
     u32x4 w = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
     if (Ly.drop.on && ok) w = dropout8(Ly.drop, (uint64_t)((int64_t)t * K + k), w);  // element t K + k
-    *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = w;
+    *reinterpret_cast<u32x4*>(xq + xsw(t, c)) = w;
   }
   const uint32_t arbytes = (uint32_t)((int64_t)r * K * 2);
   const brsrc_t ra = make_rsrc(Ly.A, arbytes);
@@ -210,15 +214,16 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
   uint8_t* xq = lds + wave * XQB;
 
   // ---- this wave's x quarter: x[0:MP][k0 + kq : + QK] (zeros past M or K);
-  // load t covers token row t, 64 chunks = 1 KB contiguous ----
+  // load i covers token rows XRPL i .. + XRPL - 1, each QK * 2 bytes contiguous ----
   const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
   const brsrc_t rx = make_rsrc(Ly.x, xbytes);
-  u32x4 xr[MP];
+  u32x4 xr[MP / sm::XRPL];
 #pragma unroll
-  for (int t = 0; t < MP; ++t) {
-    const int64_t k = k0 + kq + 8 * lane;
+  for (int i = 0; i < MP / sm::XRPL; ++i) {
+    const int t = sm::XRPL * i + lane / sm::XCPR;
+    const int64_t k = k0 + kq + 8 * (lane % sm::XCPR);
     const bool ok = t < M && k < K;
-    xr[t] = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
+    xr[i] = bload128(rx, ok ? (uint32_t)(((int64_t)t * K + k) * 2) : xbytes);
   }
 
   // ---- codes of this wave: lane's 64-weight block for (feature block b, piece p)
@@ -261,7 +266,8 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
   constexpr bool kXReg = TB == 1;
   u32x4 xf[kXReg ? sm::kPW * 8 : 1];
 #pragma unroll
-  for (int t = 0; t < MP; ++t) *reinterpret_cast<u32x4*>(xq + xsw(t, lane)) = xr[t];
+  for (int i = 0; i < MP / sm::XRPL; ++i)
+    *reinterpret_cast<u32x4*>(xq + xsw(sm::XRPL * i + lane / sm::XCPR, lane % sm::XCPR)) = xr[i];
   if constexpr (kXReg) {
 #pragma unroll
     for (int j = 0; j < sm::kPW * 8; ++j)
@@ -299,33 +305,42 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(SmallArgs a, Nf4Table ta
     }
   }
 
-  // ---- reduce the four waves' partial sums through LDS (x is no longer needed) ----
-  __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(lds);   // [wave][b][tb][lane]
-#pragma unroll
-  for (int b = 0; b < FBMAX; ++b)
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      if (b < nb) red[((wave * FBMAX + b) * TB + tb) * 64 + lane] = acc[b][tb];
-  __syncthreads();
+  // ---- reduce the four waves' partial sums through LDS (x is no longer
+  // needed), FBR feature blocks per round so that the buffer fits the x
+  // quarters' LDS ----
+  constexpr int FBR = (4 * XQB) / (4 * TB * 64 * 16) < FBMAX ? (4 * XQB) / (4 * TB * 64 * 16) : FBMAX;
+  static_assert(FBR >= 1 && FBMAX % FBR == 0, "reduction rounds");
+  f32x4* red = reinterpret_cast<f32x4*>(lds);   // [wave][b - b0][tb][lane]
   float* hp = Ly.hpart + (int64_t)kc * M * m;
-  for (int idx = tid; idx < nb * TB * 64; idx += 256) {
-    const int ln = idx & 63;
-    const int tb = (idx >> 6) % TB;
-    const int b = (idx >> 6) / TB;
-    f32x4 v = red[((0 * FBMAX + b) * TB + tb) * 64 + ln];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[((w * FBMAX + b) * TB + tb) * 64 + ln];
-    // C layout: lane ln holds token 16 tb + ln % 16, features 4 (ln / 16) + e of block b
-    const int t = 16 * tb + (ln & 15);
-    const int64_t f = f_base + 16 * b + 4 * (ln >> 4);
-    if (t < M) {
-      if ((m & 3) == 0 && f + 4 <= m) {
-        *reinterpret_cast<f32x4*>(hp + (int64_t)t * m + f) = v;
-      } else {
+  for (int b0 = 0; b0 < FBMAX; b0 += FBR) {
+    if (b0 >= nb) break;
+    __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (f + e < m) hp[(int64_t)t * m + f + e] = v[e];
+    for (int b = b0; b < b0 + FBR; ++b)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        if (b < nb) red[((wave * FBR + (b - b0)) * TB + tb) * 64 + lane] = acc[b][tb];
+    __syncthreads();
+    const int nbr = nb - b0 < FBR ? nb - b0 : FBR;
+    for (int idx = tid; idx < nbr * TB * 64; idx += 256) {
+      const int ln = idx & 63;
+      const int tb = (idx >> 6) % TB;
+      const int br = (idx >> 6) / TB;
+      f32x4 v = red[((0 * FBR + br) * TB + tb) * 64 + ln];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += red[((w * FBR + br) * TB + tb) * 64 + ln];
+      // C layout: lane ln holds token 16 tb + ln % 16, features 4 (ln / 16) + e of block b
+      const int t = 16 * tb + (ln & 15);
+      const int64_t f = f_base + 16 * (b0 + br) + 4 * (ln >> 4);
+      if (t < M) {
+        if ((m & 3) == 0 && f + 4 <= m) {
+          *reinterpret_cast<f32x4*>(hp + (int64_t)t * m + f) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (f + e < m) hp[(int64_t)t * m + f + e] = v[e];
+        }
       }
     }
   }
