@@ -379,8 +379,11 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
   const int wave = tid >> 6;
   const int lr = lane & 15;
   const int lk = lane >> 4;
-  const int fs = blockIdx.x;                 // feature tile (v partial index)
-  const int ts = blockIdx.y;                 // token tile (grad_B partial index)
+  // 1D grid (either tile count can exceed the 65535 limit of a grid's y):
+  // workgroup fs + nfs ts
+  const int nfs = (int)((J + gp::FT * SF - 1) / (gp::FT * SF));
+  const int fs = (int)blockIdx.x % nfs;      // feature tile (v partial index)
+  const int ts = (int)blockIdx.x / nfs;      // token tile (grad_B partial index)
   const int64_t f0 = (int64_t)fs * gp::FT * SF;
   const int64_t t0 = (int64_t)ts * gp::TT * gp::ST;
 
@@ -689,8 +692,10 @@ __global__ __launch_bounds__(256) void lora_dropout_term_kernel(const float* __r
   __shared__ float sv[32][16 * RB + 1];
   __shared__ __align__(16) uint16_t sa[16 * RB][128];
   const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.y * 32;
-  const int64_t f0 = (int64_t)blockIdx.x * 128;
+  // 1D grid (the token tile count can exceed the 65535 limit of a grid's y)
+  const int64_t nft = (n + 127) / 128;
+  const int64_t t0 = ((int64_t)blockIdx.x / nft) * 32;
+  const int64_t f0 = ((int64_t)blockIdx.x % nft) * 128;
   for (int i = tid; i < 32 * R; i += 256) {
     const int t = i / R, q = i % R;
     sv[t][q] = t0 + t < M ? v[(t0 + t) * R + q] : 0.0f;
@@ -734,7 +739,7 @@ __global__ __launch_bounds__(256) void lora_dropout_term_kernel(const float* __r
 
 void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
                               const DropoutDev& drop, float* out, hipStream_t stream) {
-  const dim3 grid((unsigned)cdiv(n, 128), (unsigned)cdiv(M, 32));
+  const dim3 grid((unsigned)(cdiv(n, 128) * cdiv(M, 32)));
   switch (rank_blocks(R)) {
     case 1: hipLaunchKernelGGL(lora_dropout_term_kernel<1>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
     case 2: hipLaunchKernelGGL(lora_dropout_term_kernel<2>, grid, dim3(256), 0, stream, v, A, M, n, R, scale, drop, out); break;
@@ -753,7 +758,7 @@ int gpass_splits_t(int64_t M) { return (int)cdiv(M, gp::TT * gp::ST); }
 void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
                   float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream) {
   const int sf = gpass_splits_f(J, R), st = gpass_splits_t(M);
-  const dim3 grid((unsigned)sf, (unsigned)st);
+  const dim3 grid((unsigned)((int64_t)sf * st));
   if (R <= 16)
     hipLaunchKernelGGL((gpass_kernel<1, 4>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
   else
