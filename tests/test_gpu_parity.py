@@ -111,6 +111,27 @@ def test_ragged_shapes(Q, M, n, m, r, s):
     check_full(Q, inp["W"], inp, s, label=f"ragged M={M} n={n} m={m} r={r}")
 
 
+def _random_shapes(count, seed):
+    """Seeded shapes over both forward paths: M in 1..640, n a multiple of 64
+    up to 1536, m in 1..1200, r in 1..128."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        M = int(rng.integers(1, 33)) if i % 3 == 0 else int(rng.integers(33, 641))
+        out.append((M, 64 * int(rng.integers(1, 25)), int(rng.integers(1, 1201)), int(rng.integers(1, 129)),
+                    float(rng.choice([0.25, 0.5, 1.0, 2.0, 3.0]))))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(12, 2026)
+
+
+@pytest.mark.parametrize("M,n,m,r,s", RANDOM_SHAPES)
+def test_random_shapes(Q, M, n, m, r, s):
+    inp = QI.custom_inputs(seed=M + 3 * n + 5 * m + 7 * r, M=M, n=n, m=m, r=r)
+    check_full(Q, inp["W"], inp, s, label=f"random M={M} n={n} m={m} r={r}")
+
+
 K_SPLIT = [
     # (M, n, m, r, s): more 256 x 256 output tiles than CUs, with at most half
     # a round left over: those last tiles run as two K halves whose fp32 sums
