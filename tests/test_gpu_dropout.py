@@ -103,6 +103,27 @@ def test_dropout_matches_oracle(Q, M, n, m, r, s, p, seed, offset):
         assert_close(f64(host_bits(gB2)), ref["grad_B"], f"dropout M={M} grad_B (u recomputed)")
 
 
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        M = int(rng.integers(1, 33)) if i % 2 == 0 else int(rng.integers(33, 400))
+        out.append((M, 64 * int(rng.integers(1, 17)), int(rng.integers(1, 900)), int(rng.integers(1, 129)),
+                    float(rng.choice([0.5, 1.0, 2.0])), float(rng.choice([0.1, 0.3, 0.5])),
+                    int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40))))
+    return out
+
+
+@pytest.mark.parametrize("M,n,m,r,s,p,seed,offset", _random_cases(6, 77))
+def test_dropout_random_shapes(Q, M, n, m, r, s, p, seed, offset):
+    p = f32(p)
+    inp = QI.custom_inputs(seed=900 + M + n + r, M=M, n=n, m=m, r=r)
+    say(f"dropout random M={M} n={n} m={m} r={r} p={p}")
+    got = gpu_case(Q, inp, s, (p, seed, offset))
+    ref = oracle_case(inp, s, p, seed, offset)
+    check_against_oracle(got, ref, f"dropout random M={M} n={n} m={m} r={r}")
+
+
 @pytest.mark.parametrize("M", [16, 300])
 def test_p_zero_is_the_plain_layer(Q, M):
     inp = QI.custom_inputs(seed=61, M=M, n=256, m=192, r=16)
