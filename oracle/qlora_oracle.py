@@ -127,6 +127,40 @@ def uniform4_table():
 UNIFORM4_Q, UNIFORM4_T = uniform4_table()
 
 
+def edge_mean_levels(k: int = 4) -> np.ndarray:
+    """Unnormalized levels of the [P4] Innovation 1 construction, float64:
+    level i (i = 0 .. 2^k - 1) is the mean of the normal quantiles at its
+    bucket's edges i / 2^k and (i + 1) / 2^k.
+
+    As printed the two outermost edges, probabilities 0 and 1, have infinite
+    quantiles.  Reading taken here: those two edges move to the outer
+    buckets' midpoints 1 / 2^(k+1) and 1 - 1 / 2^(k+1) (where [P1] Eq. 2
+    puts its end levels); every inner edge stays.  The construction is
+    symmetric about probability 1/2, so the upper half is computed and the
+    lower half mirrored.
+    """
+    nd = statistics.NormalDist(0.0, 1.0)
+    n = 2 ** k
+    def edge(i):
+        if i == n:
+            return 1.0 - 0.5 / n
+        return i / n
+    upper = [0.5 * (nd.inv_cdf(edge(i)) + nd.inv_cdf(edge(i + 1))) for i in range(n // 2, n)]
+    return np.array([-v for v in reversed(upper)] + upper, dtype=np.float64)
+
+
+def edge_mean_table():
+    """Return (Q, T) for edge_mean_levels: levels normalized by the largest
+    to span [-1, 1], fp32 midpoints as for NF4."""
+    q = edge_mean_levels(4)
+    Q = (q / q[-1]).astype(np.float32)
+    T = ((Q[:-1].astype(np.float64) + Q[1:].astype(np.float64)) / 2.0).astype(np.float32)
+    return Q, T
+
+
+EDGE_MEAN_Q, EDGE_MEAN_T = edge_mean_table()
+
+
 # --------------------------------------------------------------------------
 # The 8-bit float used for the double-quantized constants
 # ([P1] Step 2 "8-bit floats"; [P1] figure "scales stored in FP8";

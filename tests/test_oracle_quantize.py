@@ -307,3 +307,72 @@ def test_uniform4_error_above_nf4_and_near_int4():
     assert errs["nf4"] < errs["uniform4"]
     e_int4 = rel(O.int4_absmax_roundtrip(W))
     assert abs(errs["uniform4"] - e_int4) < 0.25 * e_int4
+
+
+# ------------------------------------------------- edge-mean (quantile-average) table
+
+def _phi(x):
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def test_edge_mean_table_shape():
+    Q, T = O.edge_mean_table()
+    assert Q[15] == 1.0 and Q[0] == -1.0
+    for j in range(16):
+        assert Q[15 - j] == -Q[j]
+    assert np.all(np.diff(Q.astype(np.float64)) > 0)
+    assert T[7] == 0.0
+    for j in range(15):
+        assert T[j] == np.float32((float(Q[j]) + float(Q[j + 1])) / 2.0)
+
+
+def test_edge_mean_levels_sit_in_their_buckets():
+    # level i lies strictly inside its equal-probability bucket (the outer
+    # buckets cut at their midpoints), checked through the normal CDF itself
+    q = O.edge_mean_levels(4)
+    edges = [i / 16 for i in range(17)]
+    edges[0], edges[16] = 1 / 32, 31 / 32
+    for i in range(16):
+        assert edges[i] < _phi(float(q[i])) < edges[i + 1], i
+
+
+def test_edge_mean_levels_exceed_bucket_midpoint_quantiles():
+    # the mean of the two edge quantiles of an inner bucket above 1/2 exceeds
+    # the quantile of the bucket's mid probability (the quantile function is
+    # strictly convex there), and mirrors below 1/2; an implementation that
+    # took the midpoint's quantile (the Eq. 2 level) would tie
+    q = O.edge_mean_levels(4)
+    p1 = O.nf4_levels(4)
+    for i in range(8, 15):
+        assert q[i] > p1[i] + 1e-6, i
+        assert q[15 - i] < p1[15 - i] - 1e-6, i
+
+
+def test_edge_mean_threshold_rule_equals_nearest_level():
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    table = O.edge_mean_table()
+    qw = O.quantize_nf4_dq(W, table=table)
+    got = O.unpack_codes(qw["codes"], W.size).astype(np.int64)
+    want = brute_nearest_codes(W, O.EDGE_MEAN_Q)
+    diff = np.nonzero(got != want)[0]
+    wb = W.reshape(-1)
+    c1 = np.repeat(qw["c1"], 64)
+    for i in diff:
+        what = np.float32(wb[i]) / np.float32(c1[i])
+        assert np.min(np.abs(O.EDGE_MEAN_T.astype(np.float64) - float(what))) <= float(np.spacing(np.float32(what)))
+    assert len(diff) <= 2
+
+
+def test_edge_mean_error_close_to_nf4_below_uniform():
+    rng = np.random.default_rng(15)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+    w64 = W.reshape(-1).astype(np.float64)
+    rel = lambda a: np.linalg.norm(a - w64) / np.linalg.norm(w64)  # noqa: E731
+    errs = {}
+    for name, table in (("nf4", None), ("uniform4", O.uniform4_table()), ("edge", O.edge_mean_table())):
+        qw = O.quantize_nf4_dq(W, table=table)
+        deq = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table))
+        errs[name] = rel(deq)
+    assert errs["edge"] < errs["uniform4"]
+    assert abs(errs["edge"] - errs["nf4"]) < 0.05 * errs["nf4"]
