@@ -164,11 +164,12 @@ def merge_bytes(m, n, r):
 
 
 def level_table_variants(Q, W, q, reps):
-    """Round-trip error of the gate weight through quantize + dequant for NF4 and the uniform grid."""
+    """Round-trip error of the gate weight through quantize + dequant for NF4, the
+    uniform grid and the edge-mean table."""
     import torch
     w = W.double()
     out = {}
-    for name, qtype in (("nf4", Q.QTYPE_NF4), ("uniform4", Q.QTYPE_UNIFORM4)):
+    for name, qtype in (("nf4", Q.QTYPE_NF4), ("uniform4", Q.QTYPE_UNIFORM4), ("edge_mean4", Q.QTYPE_EDGE_MEAN4)):
         qq = Q.quantize_dq(W, qtype=qtype)
         d = Q.dequant_dq(qq, qtype=qtype).double()
         out[name] = {"roundtrip_rel_l2": round(float(torch.linalg.norm(d - w) / torch.linalg.norm(w)), 6)}

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     QLORA_OP_FWD,
     QTYPE_NF4,
     QTYPE_UNIFORM4,
+    QTYPE_EDGE_MEAN4,
     QuantizedWeight,
     AdamStep,
     adam_step,

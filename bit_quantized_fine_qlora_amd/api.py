@@ -53,6 +53,7 @@ def _need(t: torch.Tensor, dtype, shape, name: str):
 
 QTYPE_NF4 = 0
 QTYPE_UNIFORM4 = 1
+QTYPE_EDGE_MEAN4 = 2
 
 
 def level_table(qtype: int = QTYPE_NF4):

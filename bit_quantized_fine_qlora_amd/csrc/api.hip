@@ -95,11 +95,23 @@ double normal_quantile(double p) {
 // 16 levels, symmetric (Q[15 - j] = -Q[j]), and the fp32 midpoints.
 //   qtype 0 (NF4): q_i = Phi^-1((i - 1/2)/16) / q_16
 //   qtype 1 (uniform 4-bit comparison grid): (2j - 15)/15, no zero level
+//   qtype 2 (edge-mean table, "QLoRA & 4-bit Fine-Tuning" Innovation 1):
+//     level i is the mean of Phi^-1 at its bucket's edges i/16 and
+//     (i + 1)/16, with the two outermost edges (infinite quantiles) moved to
+//     the outer buckets' midpoints 1/32 and 31/32; normalized by the largest
 Nf4Table build_table(int qtype) {
   Nf4Table t;
   double q[16];
   if (qtype == 0) {
     for (int i = 1; i <= 16; ++i) q[i - 1] = normal_quantile((i - 0.5) / 16.0);
+    for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
+  } else if (qtype == 2) {
+    double qe[17];
+    for (int i = 0; i <= 16; ++i) {
+      const double e = i == 0 ? 0.5 / 16.0 : (i == 16 ? 1.0 - 0.5 / 16.0 : i / 16.0);
+      qe[i] = normal_quantile(e);
+    }
+    for (int j = 0; j < 16; ++j) q[j] = 0.5 * (qe[j] + qe[j + 1]);
     for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
   } else {
     for (int j = 0; j < 16; ++j) t.q[j] = (float)((2.0 * j - 15.0) / 15.0);
@@ -126,8 +138,14 @@ Nf4Table build_table(int qtype) {
 const Nf4Table& table(int qtype = 0) {
   static const Nf4Table u = build_table(1);
   if (qtype == 1) return u;
+  static const Nf4Table e = build_table(2);
+  if (qtype == 2) return e;
   static const Nf4Table t = build_table(0);
   return t;
+}
+
+bool valid_qtype(int32_t qtype) {
+  return qtype == QLORA_QTYPE_NF4 || qtype == QLORA_QTYPE_UNIFORM4 || qtype == QLORA_QTYPE_EDGE_MEAN4;
 }
 
 // ---------------------------------------------------------------------------
@@ -320,7 +338,7 @@ void qlora_nf4_table(float* levels, float* thresholds) {
 }
 
 qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds) {
-  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  if (!valid_qtype(qtype)) return QLORA_ERR_VALUE;
   const Nf4Table& t = table(qtype);
   if (levels) std::memcpy(levels, t.q, sizeof(t.q));
   if (thresholds) std::memcpy(thresholds, t.t, sizeof(t.t));
@@ -329,7 +347,7 @@ qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds) 
 
 qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t n, uint8_t* codes,
                                uint8_t* absmax8, float* c2, qlora_stream_t stream) {
-  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  if (!valid_qtype(qtype)) return QLORA_ERR_VALUE;
   if (!W || !codes || !absmax8 || !c2) return QLORA_ERR_NULL;
   qlora_status st = check_weight_shape(m, n);
   if (st != QLORA_OK) return st;
@@ -344,7 +362,7 @@ qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t
 
 qlora_status qlora_dequant_dq(int32_t qtype, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                               int64_t m, int64_t n, qlora_bf16* W_out, qlora_stream_t stream) {
-  if (qtype != QLORA_QTYPE_NF4 && qtype != QLORA_QTYPE_UNIFORM4) return QLORA_ERR_VALUE;
+  if (!valid_qtype(qtype)) return QLORA_ERR_VALUE;
   if (!codes || !absmax8 || !c2 || !W_out) return QLORA_ERR_NULL;
   qlora_status st = check_weight_shape(m, n);
   if (st != QLORA_OK) return st;

@@ -162,8 +162,9 @@ qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, fl
                              float eps, float weight_decay, int64_t step, qlora_stream_t stream);
 
 /* Level tables for qlora_quantize_dq / qlora_dequant_dq / qlora_level_table. */
-#define QLORA_QTYPE_NF4 0      /* the NF4 levels above */
-#define QLORA_QTYPE_UNIFORM4 1 /* uniform 4-bit grid (2j - 15)/15, j = 0..15 */
+#define QLORA_QTYPE_NF4 0        /* the NF4 levels above */
+#define QLORA_QTYPE_UNIFORM4 1   /* uniform 4-bit grid (2j - 15)/15, j = 0..15 */
+#define QLORA_QTYPE_EDGE_MEAN4 2 /* mean of each bucket's edge quantiles (below) */
 
 /*
  * The 16 levels and 15 thresholds of a level table (host outputs, either
@@ -172,7 +173,13 @@ qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, fl
  * Innovation 1 (NF4 versus uniform 4-bit quantization of normal weights):
  * 16 evenly spaced levels over [-1, 1] without a zero level, symmetric like
  * the NF4 table so the same code layout and kernels apply; thresholds are
- * the fp32 midpoints.  QLORA_ERR_VALUE for an unknown qtype.
+ * the fp32 midpoints.  QLORA_QTYPE_EDGE_MEAN4 is the other normal-quantile
+ * construction, of "QLoRA & 4-bit Fine-Tuning" Innovation 1: level i is the
+ * mean of the normal quantiles at its bucket's edges i/16 and (i + 1)/16;
+ * as printed the outermost edges (probabilities 0 and 1) have infinite
+ * quantiles, so they are moved to the outer buckets' midpoints 1/32 and
+ * 31/32, and the levels are normalized by the largest.  QLORA_ERR_VALUE for
+ * an unknown qtype.
  */
 qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds);
 

@@ -52,13 +52,14 @@ def test_library_table_matches_oracle(lib):
 
 
 def test_level_tables_match_oracle(lib):
-    for qtype, (Q, T) in ((0, (O.NF4_Q, O.NF4_T)), (1, (O.UNIFORM4_Q, O.UNIFORM4_T))):
+    for qtype, (Q, T) in ((0, (O.NF4_Q, O.NF4_T)), (1, (O.UNIFORM4_Q, O.UNIFORM4_T)),
+                          (2, (O.EDGE_MEAN_Q, O.EDGE_MEAN_T))):
         lv = (ctypes.c_float * 16)()
         th = (ctypes.c_float * 15)()
         assert lib.qlora_level_table(qtype, ctypes.cast(lv, ctypes.c_void_p), ctypes.cast(th, ctypes.c_void_p)) == 0
         assert np.array_equal(np.frombuffer(lv, dtype=np.float32).view(np.uint32), Q.view(np.uint32)), qtype
         assert np.array_equal(np.frombuffer(th, dtype=np.float32).view(np.uint32), T.view(np.uint32)), qtype
-    assert lib.qlora_level_table(2, None, None) == -7
+    assert lib.qlora_level_table(3, None, None) == -7
 
 
 def test_status_strings(lib):

@@ -360,6 +360,24 @@ def test_uniform4_quantizer(Q, m, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("m,n", UNIFORM4)
+def test_edge_mean_quantizer(Q, m, n):
+    # the edge-mean (quantile-average) table through the same kernels: bit-exact
+    inp = QI.custom_inputs(seed=m + 3 * n, M=1, n=n, m=m, r=1)
+    W = inp["W"]
+    table = O.edge_mean_table()
+    say(f"edge-mean quantize {m}x{n}")
+    q = Q.quantize_dq(torch.from_numpy(W).cuda(), qtype=Q.QTYPE_EDGE_MEAN4)
+    torch.cuda.synchronize()
+    qw = O.quantize_nf4_dq(W, table=table)
+    check_quantizer(q, qw)
+    deq = host_bits(Q.dequant_dq(q, qtype=Q.QTYPE_EDGE_MEAN4)).reshape(-1)
+    want = O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table)
+    assert np.array_equal(deq, want), "edge-mean dequantized weight differs"
+    del q
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ adapter merge
 
 def bf16_order(bits):
