@@ -517,6 +517,12 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's writes are done
   __builtin_amdgcn_wave_barrier();
   const bool vec_ok = (p.N & 7) == 0;
+  // Whole-row stores carry the non-temporal hint (and sc0): the output is
+  // not read again by this kernel, and streaming it past the caches keeps
+  // the last-level cache for the next kernel's input (the g pass after the
+  // forward ran 46 -> 41 us, the step 1.7 % faster).  M N 2 < 2^31 bytes.
+  const brsrc_t r_out = make_rsrc(p.out, (uint32_t)(p.M * p.N * 2));
+  constexpr int kAuxStream = 3;  // buffer cache policy: sc0 | nt
   const int c = lane % CPR;
   const int64_t f = f0 + wf + 8 * c;
 #pragma unroll
@@ -527,7 +533,7 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
     if (t >= p.M || f >= p.N) continue;
     uint16_t* dst = p.out + t * p.N + f;
     if (vec_ok && f + 8 <= p.N) {
-      *reinterpret_cast<u32x4*>(dst) = v;
+      __builtin_amdgcn_raw_buffer_store_b128(v, r_out, (int)((t * p.N + f) * 2), 0, kAuxStream);
     } else {
       for (int e = 0; e < 8; ++e)
         if (f + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
