@@ -77,22 +77,32 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   }
   __syncthreads();
 
-#pragma unroll 1
+  // The next pass's 64 bytes per lane are loaded before this pass's
+  // arithmetic, so each lane keeps two passes of loads in flight.
+  float4 wq[2][4];
+  auto load_pass = [&](int pass, float4 (&dst)[4]) {
+    const int lb = pass * 64 + (tid >> 2);
+    if (lb < nb) {
+      const float4* src = reinterpret_cast<const float4*>(W + (blk0 + lb) * kBlock + (tid & 3) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_pass(0, wq[0]);
+#pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int lb = pass * 64 + (tid >> 2);
     const int quarter = tid & 3;
     const bool valid = lb < nb;
+    if (pass + 1 < 4) load_pass(pass + 1, wq[(pass + 1) & 1]);
     float w[16];
-    if (valid) {
-      const float4* src = reinterpret_cast<const float4*>(W + (blk0 + lb) * kBlock + quarter * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 t = src[i];
-        w[4 * i + 0] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) w[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = wq[pass & 1][i];
+      w[4 * i + 0] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
     }
     float a = 0.0f;
 #pragma unroll
