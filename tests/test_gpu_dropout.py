@@ -214,3 +214,33 @@ def test_full_size_layer_sampled(Q):
     assert_close(f64(host_bits(got["grad_B"][rc])), gB_ref, "dropout full grad_B (sampled)")
     del got
     torch.cuda.empty_cache()
+
+
+def test_many_tokens_sampled(Q):
+    # 2.2 M tokens of a narrow layer: more 32-token tiles than a grid's y
+    # dimension allows (65535), so the dropout term and the g pass must
+    # launch 1D grids; checked on sampled tokens
+    M, n, m, r, s = 2_200_000, 64, 64, 8, 2.0
+    p, seed, offset = f32(0.2), 4242, 17
+    say(f"dropout many tokens M={M} n={n} m={m} r={r}")
+    rng = np.random.default_rng(5)
+    x_bits = QI.to_bf16_bits(rng.standard_normal((M, n), dtype=np.float32))
+    g_bits = QI.to_bf16_bits(rng.standard_normal((M, m), dtype=np.float32))
+    inp = QI.custom_inputs(seed=3, M=1, n=n, m=m, r=r)
+    inp["x"], inp["g"] = x_bits, g_bits
+    got = gpu_case(Q, inp, s, (p, seed, offset))
+    qw = O.quantize_nf4_dq(inp["W"])
+    Wd = f64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], m * n)).reshape(m, n)
+    toks = sample_indices(M, 64, 21)
+    keep = O.dropout_mask_at(toks, np.arange(n), n, p, seed, offset)
+    x, g = f64(x_bits[toks]), f64(g_bits[toks])
+    A, B = f64(inp["A"]), f64(inp["B"])
+    u = (x * keep / (1 - p)) @ A.T
+    v = g @ B
+    tc = torch.from_numpy(toks).cuda()
+    assert_close(f64(host_bits(got["h"][tc])), x @ Wd.T + s * (u @ B.T), "many tokens h (sampled)")
+    assert_close(got["u"][tc].cpu().numpy(), u, "many tokens u (sampled)")
+    assert_close(f64(host_bits(got["grad_x"][tc])), g @ Wd + s * (v @ A) * keep / (1 - p),
+                 "many tokens grad_x (sampled)")
+    del got
+    torch.cuda.empty_cache()
