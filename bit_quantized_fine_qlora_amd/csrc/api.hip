@@ -251,9 +251,10 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, ksplit, total;
   int su, sv, sa, sb;
   bool gpass;     // v and grad_B from one read of g
+  bool has_ksplit;
   int64_t m_pad;  // row length of g as the kernels read it
 };
 
@@ -281,6 +282,10 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
   // dropout: the masked adapter part of grad_x in fp32
   w.dterm = dropout ? L.take((size_t)M * n * sizeof(float)) : 0;
+  // grad_x GEMM tiles split in K (few tiles, or a short last round)
+  const size_t kb = gemm_split_ws_bytes(M, n, w.m_pad);
+  w.ksplit = kb ? L.take(kb) : 0;
+  w.has_ksplit = kb != 0;
   w.total = L.total;
   return w;
 }
@@ -646,11 +651,12 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
         launch_lora_dropout_term(v, A, M, n, r, s * inv_keep, dd, dterm, hs);
       }
       Timed tm("dgrad_gemm", hs);
-      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, 0, s, nullptr, table(), hs, dterm);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, 0, s,
+                        w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs, dterm);
     } else {
       Timed tm("dgrad_gemm", hs);
-      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, nullptr, table(), hs,
-                        nullptr);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s,
+                        w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs, nullptr);
     }
   }
   return hip_status();

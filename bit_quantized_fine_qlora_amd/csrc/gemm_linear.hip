@@ -611,7 +611,11 @@ int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
   const int cus = device_cus();
   const int64_t rem = tiles % cus;
   const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
-  if (tiles < cus || rem == 0 || rem > cus / 2 || nk < 8) return 0;
+  if (nk < 8) return 0;
+  // Few tiles (at most half the CUs, e.g. 33..256 tokens): every tile runs as
+  // two K halves, so twice as many CUs stream the weight.
+  if (tiles * 2 <= cus) return (int)tiles;
+  if (tiles < cus || rem == 0 || rem > cus / 2) return 0;
   return (int)rem;
 }
 
