@@ -97,7 +97,16 @@ struct GemmArgs {
   float* partial;         // nsplit x 256 x 256 fp32, the first finisher's sum
   uint32_t* split_sync;   // nsplit x {arrivals, partial ready}, zero at launch
   const float* add;       // M x N fp32 added before the rounding, or null
+  // Few tiles (see gemm_pieces): pieces > 1 runs every tile as that many K
+  // pieces, work item b being piece b % pieces of tile b / pieces; each piece
+  // writes its fp32 sum to plane b % pieces of piece_out (planes of M x N,
+  // piece_plane(M, N) apart) and reduce_pieces_kernel finishes the output.
+  int pieces;
+  float* piece_out;
 };
+
+// Elements between the K-piece planes: M N rounded up to 64 (256 bytes).
+__host__ __device__ __forceinline__ int64_t piece_plane(int64_t M, int64_t N) { return (M * N + 63) & ~(int64_t)63; }
 
 // The two halves of a split tile meet at the end: the first to finish
 // (by an atomic arrival count) stores its fp32 accumulators and raises the
@@ -435,6 +444,30 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
     if (ks + 1 < nsteps) step(ks + 1, lds.w[1], lds.a[1], lds.a[0]);
   }
 
+  if (p.pieces > 1) {
+    // one K piece: its fp32 sum, row-major, in the piece's own plane (rows
+    // past M are dropped by the range check; M N 4 < 2^32 bytes here)
+    const uint32_t plane_bytes = (uint32_t)(p.M * p.N * 4);
+    float* plane = p.piece_out + (size_t)((int)blockIdx.x % p.pieces) * (size_t)piece_plane(p.M, p.N);
+    const brsrc_t r_pl = make_rsrc(plane, plane_bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t t = t0 + wt + 16 * j + lr;
+        const int64_t f = f0 + wf + 16 * i + 4 * lq;
+        if (f + 4 <= p.N) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r_pl,
+                                                 (int)(t < p.M ? (uint32_t)((t * p.N + f) * 4) : plane_bytes), 0, 0);
+        } else if (t < p.M) {
+          for (int e = 0; e < 4; ++e)
+            if (f + e < p.N) plane[t * p.N + f + e] = acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
+
   // Split tile: arrival order decides who stores its sum and who finishes.
   // The finisher adds the stored sum through a buffer resource that is empty
   // (every load reads 0) for whole tiles, so all paths run the same in-place
@@ -563,7 +596,13 @@ __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, 
   // the K halves of the split tiles, which run in the last round
   int tile, k0 = 0, ks = nk, split = 0;
   bool lora = true;
-  if ((int)blockIdx.x < p.full_tiles) {
+  if (p.pieces > 1) {
+    const int piece = (int)blockIdx.x % p.pieces;
+    tile = (int)blockIdx.x / p.pieces;
+    k0 = piece * nk / p.pieces;
+    ks = (piece + 1) * nk / p.pieces - k0;
+    lora = piece == p.pieces - 1;
+  } else if ((int)blockIdx.x < p.full_tiles) {
     tile = xcd_remap_l(blockIdx.x, p.full_tiles);
   } else {
     const int w = (int)blockIdx.x - p.full_tiles;
@@ -612,14 +651,53 @@ int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
   const int64_t rem = tiles % cus;
   const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
   if (nk < 8) return 0;
-  // Few tiles (at most half the CUs, e.g. 33..256 tokens): every tile runs as
-  // two K halves, so twice as many CUs stream the weight.
-  if (tiles * 2 <= cus) return (int)tiles;
   if (tiles < cus || rem == 0 || rem > cus / 2) return 0;
   return (int)rem;
 }
 
+// Few tiles (at most half the CUs, e.g. 33..256 tokens at 4096 - 14336
+// features): every tile runs as P K pieces, P = min(CUs / tiles, 16) with
+// at least 8 K steps per piece, so up to all CUs stream the weight.  The P
+// fp32 planes (P M N 4 <= 4 CUs 2^16 4 bytes) are summed in piece order by
+// a separate pass, so the result does not depend on which piece ends first.
+constexpr int kMaxPieces = 16;
+int gemm_pieces(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT);
+  const int cus = device_cus();
+  const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
+  if (tiles * 2 > cus) return 1;
+  int64_t pc = cus / tiles;
+  if (pc > kMaxPieces) pc = kMaxPieces;
+  while (pc > 1 && nk / pc < 8) --pc;
+  return (int)pc;
+}
+
+// out[i] = bf16(((plane 0 + plane 1) + ...) + add[i]), 4 elements a thread;
+// planes `stride` elements apart (a multiple of 64).
+__global__ __launch_bounds__(256) void reduce_pieces_kernel(const float* __restrict__ planes, int pieces,
+                                                            int64_t count, int64_t stride,
+                                                            const float* __restrict__ add,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  if (i + 4 <= count) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(planes + i);
+    for (int q = 1; q < pieces; ++q) v += *reinterpret_cast<const f32x4*>(planes + (size_t)q * stride + i);
+    if (add) v += *reinterpret_cast<const f32x4*>(add + i);
+    *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    return;
+  }
+  for (int64_t e = i; e < count; ++e) {
+    float v = planes[e];
+    for (int q = 1; q < pieces; ++q) v += planes[(size_t)q * stride + e];
+    if (add) v += add[e];
+    out[e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+  }
+}
+
 size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const int pc = gemm_pieces(M, N, K);
+  if (pc > 1) return (size_t)pc * piece_plane(M, N) * sizeof(float);
   const size_t ns = (size_t)gemm_split_tiles(M, N, K);
   if (!ns) return 0;
   return ns * lg2::BF * lg2::BT * sizeof(float) + ((2 * ns * sizeof(uint32_t) + 255) / 256) * 256;
@@ -633,6 +711,23 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
   p.tiles_f = (int)((p.N + lg2::BF - 1) / lg2::BF);
   p.tiles_t = (int)((p.M + lg2::BT - 1) / lg2::BT);
   const int tiles = p.tiles_f * p.tiles_t;
+  const int pc = split_ws ? gemm_pieces(p.M, p.N, p.K) : 1;
+  if (pc > 1) {
+    p.pieces = pc;
+    p.piece_out = static_cast<float*>(split_ws);
+    p.full_tiles = tiles;
+    p.nsplit = 0;
+    p.partial = nullptr;
+    p.split_sync = nullptr;
+    if (bwd)
+      hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
+    else
+      hipLaunchKernelGGL(linear_gemm_kernel<false>, dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
+    const int64_t count = p.M * p.N;
+    hipLaunchKernelGGL(reduce_pieces_kernel, dim3((unsigned)((count + 1023) / 1024)), dim3(256), 0, stream,
+                       p.piece_out, pc, count, piece_plane(p.M, p.N), p.add, p.out);
+    return;
+  }
   const int ns = split_ws ? gemm_split_tiles(p.M, p.N, p.K) : 0;
   p.full_tiles = tiles - ns;
   p.nsplit = ns;

@@ -79,6 +79,7 @@ CASES = [
     (300, 512, 320, 8, 2.0, 0.05, 99, 2 ** 32 - 100),      # tiled; counters carry into the high word
     (128, 384, 256, 32, 1.0, 0.2, 77, 3),                  # rank 32 (v and grad_B in one pass over g)
     (256, 256, 512, 64, 0.5, 0.5, 5, 0),                   # rank 64 (separate v and grad_B kernels)
+    (64, 512, 2048, 16, 2.0, 0.1, 4321, 5),                # grad_x GEMM in 4 K pieces, masked term added after
 ]
 
 

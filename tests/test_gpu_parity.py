@@ -160,6 +160,35 @@ def test_k_split_last_round(Q, M, n, m, r, s):
         assert torch.equal(h2, got["h"]) and torch.equal(u2, got["u"])
 
 
+FEW_TILES = [
+    # (M, n, m, r, s) with at most half as many 256 x 256 output tiles as
+    # CUs: every tile runs as P K pieces whose fp32 planes a second pass adds
+    # in piece order.  P (forward / grad_x on 256 CUs): 4 / 5 with ragged
+    # features (m % 4 != 0, M m odd); 4 / 9 with two LoRA steps in the last
+    # piece; 2 / 16; 8 / 1 (too few K steps to split the grad_x GEMM).
+    (200, 2048, 3001, 16, 2.0),
+    (96, 2048, 5000, 40, 0.5),
+    (256, 1024, 8192, 8, 1.0),
+    (33, 4096, 512, 16, 2.0),
+]
+
+
+@pytest.mark.parametrize("M,n,m,r,s", FEW_TILES)
+def test_k_pieces_few_tiles(Q, M, n, m, r, s):
+    lib = Q._lib.load()
+    tiles = -(-M // 256) * -(-m // 256)
+    assert lib.qlora_workspace_bytes(0, M, n, m, r) >= 2 * M * m * 4 or tiles * 2 > 256, "K-piece planes not in the workspace"
+    inp = QI.custom_inputs(seed=7 * M + m + 11 * r, M=M, n=n, m=m, r=r)
+    got, _ = check_full(Q, inp["W"], inp, s, label=f"k-pieces M={M} n={n} m={m} r={r}")
+    say("k-pieces determinism")
+    for _ in range(2):
+        h2, u2 = Q.linear_fwd(got["x"], got["q"], got["A"], got["B"], s)
+        gx2, gA2, gB2 = Q.linear_bwd(got["x"], got["g"], got["q"], got["A"], got["B"], s, u=u2)
+        torch.cuda.synchronize()
+        assert torch.equal(h2, got["h"]) and torch.equal(u2, got["u"])
+        assert torch.equal(gx2, got["grad_x"]) and torch.equal(gA2, got["grad_A"]) and torch.equal(gB2, got["grad_B"])
+
+
 SMALL_M = [
     # (M, n, m, r, s) on the weight-streaming path (M <= 32): K chunks of 2048,
     # 256-k pieces per wave, groups of 128 features
