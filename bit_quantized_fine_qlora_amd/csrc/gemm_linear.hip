@@ -99,14 +99,12 @@ struct GemmArgs {
   const float* add;       // M x N fp32 added before the rounding, or null
   // Few tiles (see gemm_pieces): pieces > 1 runs every tile as that many K
   // pieces, work item b being piece b % pieces of tile b / pieces; each piece
-  // writes its fp32 sum to plane b % pieces of piece_out (planes of M x N,
-  // piece_plane(M, N) apart) and reduce_pieces_kernel finishes the output.
+  // writes its fp32 sums to slot b of piece_out (256 x 256 floats a slot, in
+  // the split hand-off's fragment layout) and reduce_pieces_kernel finishes
+  // the output.
   int pieces;
   float* piece_out;
 };
-
-// Elements between the K-piece planes: M N rounded up to 64 (256 bytes).
-__host__ __device__ __forceinline__ int64_t piece_plane(int64_t M, int64_t N) { return (M * N + 63) & ~(int64_t)63; }
 
 // The two halves of a split tile meet at the end: the first to finish
 // (by an atomic arrival count) stores its fp32 accumulators and raises the
@@ -324,7 +322,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
 // 128 x 64 in the forward and 64 x 128 in the backward, where the W'
 // fragments come from half-rate transposed reads and the activation
 // fragments from full-rate ones (the 64 x 128 shape halves the former).
-template <bool kBwd>
+template <bool kBwd, bool kPieces>
 __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds& lds, int tid, int64_t f0,
                                               int64_t t0, int k0, int nk, bool lora, int split, uint32_t* lds_word) {
   constexpr int WF = kBwd ? 64 : 128;
@@ -444,30 +442,6 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
     if (ks + 1 < nsteps) step(ks + 1, lds.w[1], lds.a[1], lds.a[0]);
   }
 
-  if (p.pieces > 1) {
-    // one K piece: its fp32 sum, row-major, in the piece's own plane (rows
-    // past M are dropped by the range check; M N 4 < 2^32 bytes here)
-    const uint32_t plane_bytes = (uint32_t)(p.M * p.N * 4);
-    float* plane = p.piece_out + (size_t)((int)blockIdx.x % p.pieces) * (size_t)piece_plane(p.M, p.N);
-    const brsrc_t r_pl = make_rsrc(plane, plane_bytes);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t t = t0 + wt + 16 * j + lr;
-        const int64_t f = f0 + wf + 16 * i + 4 * lq;
-        if (f + 4 <= p.N) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r_pl,
-                                                 (int)(t < p.M ? (uint32_t)((t * p.N + f) * 4) : plane_bytes), 0, 0);
-        } else if (t < p.M) {
-          for (int e = 0; e < 4; ++e)
-            if (f + e < p.N) plane[t * p.N + f + e] = acc[i][j][e];
-        }
-      }
-    }
-    return;
-  }
-
   // Split tile: arrival order decides who stores its sum and who finishes.
   // The finisher adds the stored sum through a buffer resource that is empty
   // (every load reads 0) for whole tiles, so all paths run the same in-place
@@ -476,6 +450,18 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   const int sidx = split ? split - 1 : 0;
   float* part_base = p.partial ? p.partial + (size_t)sidx * (lg2::BF * lg2::BT) : nullptr;
   const uint32_t poff = (uint32_t)(wave * (NI * NJ * 1024) + 16 * lane);  // [wave][i][j][lane] f32x4
+  if (kPieces) {
+    // one K piece (few-tile mode): its fp32 sums, in the layout below, in
+    // slot tile * pieces + piece (the work item's index) of piece_out
+    const brsrc_t r_pl = make_rsrc(p.piece_out + (size_t)blockIdx.x * (lg2::BF * lg2::BT), lg2::BF * lg2::BT * 4);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), r_pl,
+                                               (int)(poff + (i * NJ + j) * 1024), 0, 0);
+    return;
+  }
   if (split) {
     uint32_t* sync = p.split_sync + 2 * sidx;
     if (tid == 0) *lds_word = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -581,7 +567,9 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   }
 }
 
-template <bool kBwd>
+// kPieces: few-tile mode (every tile as p.pieces K pieces), a separate
+// instantiation so that the other kernels' register allocation is untouched.
+template <bool kBwd, bool kPieces>
 __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, Nf4Table tab) {
   using T = lg2::Tile<kBwd>;
   __shared__ __align__(16) uint8_t sw0[T::W];
@@ -596,7 +584,7 @@ __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, 
   // the K halves of the split tiles, which run in the last round
   int tile, k0 = 0, ks = nk, split = 0;
   bool lora = true;
-  if (p.pieces > 1) {
+  if (kPieces) {
     const int piece = (int)blockIdx.x % p.pieces;
     tile = (int)blockIdx.x / p.pieces;
     k0 = piece * nk / p.pieces;
@@ -621,7 +609,7 @@ __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, 
   if (tid >= 64 * lg2::kMfmaWaves)
     gemm_producer<kBwd>(p, tab, lds, tid - 64 * lg2::kMfmaWaves, f0, t0, k0, ks, lora, split, &lds_word);
   else
-    gemm_consumer<kBwd>(p, lds, tid, f0, t0, k0, ks, lora, split, &lds_word);
+    gemm_consumer<kBwd, kPieces>(p, lds, tid, f0, t0, k0, ks, lora, split, &lds_word);
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
@@ -658,11 +646,12 @@ int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
 // Few tiles (at most half the CUs, e.g. 33..256 tokens at 4096 - 14336
 // features): every tile runs as P K pieces, P = min(CUs / tiles, 16) with
 // at least 8 K steps per piece, so up to all CUs stream the weight.  The P
-// fp32 planes (P M N 4 <= 4 CUs 2^16 4 bytes) are summed in piece order by
-// a separate pass, so the result does not depend on which piece ends first.
+// fp32 tile sums (tiles P 2^18 <= CUs 2^18 bytes) are added in piece order
+// by a separate pass, so the result does not depend on which piece ends first.
 constexpr int kMaxPieces = 16;
+static int64_t tiles_of(int64_t M, int64_t N) { return ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT); }
 int gemm_pieces(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT);
+  const int64_t tiles = tiles_of(M, N);
   const int cus = device_cus();
   const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
   if (tiles * 2 > cus) return 1;
@@ -672,32 +661,46 @@ int gemm_pieces(int64_t M, int64_t N, int64_t K) {
   return (int)pc;
 }
 
-// out[i] = bf16(((plane 0 + plane 1) + ...) + add[i]), 4 elements a thread;
-// planes `stride` elements apart (a multiple of 64).
-__global__ __launch_bounds__(256) void reduce_pieces_kernel(const float* __restrict__ planes, int pieces,
-                                                            int64_t count, int64_t stride,
-                                                            const float* __restrict__ add,
-                                                            uint16_t* __restrict__ out) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= count) return;
-  if (i + 4 <= count) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(planes + i);
-    for (int q = 1; q < pieces; ++q) v += *reinterpret_cast<const f32x4*>(planes + (size_t)q * stride + i);
-    if (add) v += *reinterpret_cast<const f32x4*>(add + i);
-    *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+// Finishes a few-tile GEMM: out = bf16(((piece 0 + piece 1) + ...) + add).
+// Thread g takes fragment item g % 16384 (4 features of one token) of tile
+// g / 16384 from every piece's slot, in the consumer's [wave][i][j][lane]
+// order, so that the slot reads are whole 1 KB rows.
+template <bool kBwd>
+__global__ __launch_bounds__(256) void reduce_pieces_kernel(GemmArgs p) {
+  constexpr int WF = kBwd ? 64 : 128;
+  constexpr int WT = 128 * 64 / WF;
+  constexpr int NI = WF / 16, NJ = WT / 16;
+  constexpr int kItems = lg2::BF * lg2::BT / 4;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tile = (int)(g / kItems);
+  const int rem = (int)(g % kItems);
+  const int wave = rem / (NI * NJ * 64);
+  const int ij = (rem / 64) % (NI * NJ);
+  const int lane = rem % 64;
+  const int i = ij / NJ, j = ij % NJ;
+  const int64_t t = (int64_t)(tile / p.tiles_f) * lg2::BT + (wave / (lg2::BF / WF)) * WT + 16 * j + (lane & 15);
+  const int64_t f = (int64_t)(tile % p.tiles_f) * lg2::BF + (wave % (lg2::BF / WF)) * WF + 16 * i + 4 * (lane >> 4);
+  if (tile >= p.tiles_f * p.tiles_t || t >= p.M || f >= p.N) return;
+  const float* slot = p.piece_out + (size_t)tile * p.pieces * kItems * 4 + (size_t)rem * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(slot);
+  for (int q = 1; q < p.pieces; ++q) v += *reinterpret_cast<const f32x4*>(slot + (size_t)q * kItems * 4);
+  const int64_t o = t * p.N + f;
+  if ((p.N & 3) == 0) {
+    if (p.add) v += *reinterpret_cast<const f32x4*>(p.add + o);
+    *reinterpret_cast<u32x2*>(p.out + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     return;
   }
-  for (int64_t e = i; e < count; ++e) {
-    float v = planes[e];
-    for (int q = 1; q < pieces; ++q) v += planes[(size_t)q * stride + e];
-    if (add) v += add[e];
-    out[e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (f + e >= p.N) break;
+    const float a = v[e] + (p.add ? p.add[o + e] : 0.0f);
+    p.out[o + e] = (uint16_t)(pack_bf16x2(a, 0.0f) & 0xFFFFu);
   }
 }
 
 size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const int pc = gemm_pieces(M, N, K);
-  if (pc > 1) return (size_t)pc * piece_plane(M, N) * sizeof(float);
+  if (pc > 1) return (size_t)pc * tiles_of(M, N) * lg2::BF * lg2::BT * sizeof(float);
   const size_t ns = (size_t)gemm_split_tiles(M, N, K);
   if (!ns) return 0;
   return ns * lg2::BF * lg2::BT * sizeof(float) + ((2 * ns * sizeof(uint32_t) + 255) / 256) * 256;
@@ -720,12 +723,14 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
     p.partial = nullptr;
     p.split_sync = nullptr;
     if (bwd)
-      hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
+      hipLaunchKernelGGL((linear_gemm_kernel<true, true>), dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
     else
-      hipLaunchKernelGGL(linear_gemm_kernel<false>, dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
-    const int64_t count = p.M * p.N;
-    hipLaunchKernelGGL(reduce_pieces_kernel, dim3((unsigned)((count + 1023) / 1024)), dim3(256), 0, stream,
-                       p.piece_out, pc, count, piece_plane(p.M, p.N), p.add, p.out);
+      hipLaunchKernelGGL((linear_gemm_kernel<false, true>), dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
+    const unsigned rblocks = (unsigned)tiles * (lg2::BF * lg2::BT / 4 / 256);
+    if (bwd)
+      hipLaunchKernelGGL(reduce_pieces_kernel<true>, dim3(rblocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(reduce_pieces_kernel<false>, dim3(rblocks), dim3(256), 0, stream, p);
     return;
   }
   const int ns = split_ws ? gemm_split_tiles(p.M, p.N, p.K) : 0;
@@ -741,9 +746,9 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
   }
   const int grid = tiles + ns;
   if (bwd)
-    hipLaunchKernelGGL(linear_gemm_kernel<true>, dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
+    hipLaunchKernelGGL((linear_gemm_kernel<true, false>), dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
   else
-    hipLaunchKernelGGL(linear_gemm_kernel<false>, dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
+    hipLaunchKernelGGL((linear_gemm_kernel<false, false>), dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
 }
 
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
