@@ -142,6 +142,11 @@ def test_workspace_sizes(lib):
     # 896 output tiles on 256 CUs: the last 128 tiles run as K halves whose fp32
     # partial sums (256 x 256 each) live in the forward's workspace
     assert lib.qlora_workspace_bytes(0, 4096, 4096, 14336, 16) >= 128 * 256 * 256 * 4
+    # few tiles (256 tokens; sized for 256 CUs, the count assumed without a
+    # device): the 16 grad_x tiles run as 16 K pieces and the 56 forward tiles
+    # as 4, each piece's fp32 sums (256 x 256) in the workspace
+    assert lib.qlora_workspace_bytes(1, 256, 4096, 14336, 16) >= 16 * 16 * 256 * 256 * 4
+    assert lib.qlora_workspace_bytes(0, 256, 4096, 14336, 16) >= 56 * 4 * 256 * 256 * 4
     # 256 tiles fill the chip exactly: nothing is split
     assert lib.qlora_workspace_bytes(0, 4096, 4096, 4096, 16) < 16 << 20
     assert lib.qlora_workspace_bytes(0, 32, 100, 256, 8) == 0
