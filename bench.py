@@ -1,17 +1,27 @@
 """Benchmark of the QLoRA adapted-linear hot path on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input, already
-resident in HBM: quantize the frozen weight (NF4 + double quantization),
-forward (u = x A^T, h = x W'^T + s u B^T), backward (grad_x, grad_A,
-grad_B).  Workload: the Llama-3.1-8B-shaped gate projection, W0 14336 x
-4096, 4096 tokens (batch 4 x seq 1024), LoRA r = 16, alpha = 32.
+resident in HBM, on the 70B-shaped transformer block (hidden 8192, FFN
+28672, 64 query / 8 KV heads of dim 128; q 8192x8192, k and v 1024x8192,
+o 8192x8192, gate and up 28672x8192, down 8192x28672), 8192 tokens (batch 8
+x seq 1024), LoRA r = 64, alpha = 16 on all seven projections:
+  - quantize the seven frozen weights (NF4 + double quantization);
+  - forward of every layer (u = x A^T, h = x W'^T + s u B^T);
+  - backward of every layer, in reverse order (grad_x, grad_A, grad_B).
+Every layer has its own independent x and upstream gradient g.
 
-value = algorithmic forward + backward flops per step / step time (TFLOP/s),
-the quantizer's time included in the step.  Prints one JSON line.
+value = algorithmic forward + backward flops of the seven layers per step
+(2.855e13) / step time, the quantizer's time included in the step.  The
+timed steps run with the library's kernel timing off; per-kernel times come
+from a separate pass, layer by layer, with HIP events recorded on the stream
+the library launches on.  Prints one JSON line.
 
 Besides the timed steps (and outside them) it also measures, each with HIP
 events on the stream the library launches on:
-  - the forward alone and the backward alone of the same layer;
+  - the block's forward pass alone, backward pass alone and quantization;
+  - the 8B-shaped gate projection (14336 x 4096, 4096 tokens, r = 16) and
+    down projection (4096 x 14336, 4096 tokens, r = 64): forward, backward,
+    forward + backward and quantize;
   - the small-token regime: the forward of all seven layers of the
     8B-shaped block at 16 tokens in one grouped call, and the quantization of
     the block's seven weights, both against the HBM peak;
@@ -21,12 +31,15 @@ events on the stream the library launches on:
     adapters of a 32-layer 8B-shaped model at r = 16 (448 tensors, 41.9 M
     parameters, 28 bytes each), against the HBM peak, and over one block's
     adapters with the optimizer state in pinned host memory;
-  - the quantizer on the uniform 4-bit comparison grid: round-trip relative
-    error of the gate weight through the GPU kernels for NF4 and for the
-    uniform grid, and the uniform quantizer's time.
+  - LoRA dropout on the gate projection, against the plain passes;
+  - the quantizer on the uniform 4-bit comparison grid and the edge-mean
+    table: round-trip relative error of the gate weight through the GPU
+    kernels, and the uniform quantizer's time.
 For the HBM-bound measurements the caches are flushed before every
 repetition by reading 1 GiB (a read evicts the working set cleanly; a write
 flush would leave dirty lines whose write-back lands in the timed kernel).
+Inputs are drawn on the device with torch's generator from the same
+distributions as the seeded parity inputs (they are timed, not compared).
 """
 
 from __future__ import annotations
@@ -44,21 +57,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
-# HBM bytes per launch of the GEMM kernels on this workload, from rocprofv3
-# --pmc FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch),
-# scaled by what the same counters read for a plain 1 GiB device copy
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/).  Valid only for the
-# GEMM sources they were taken on (the kernel and the header it includes):
-# reported as null once either changes.
+# HBM bytes per launch of the dominant GEMM kernels, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs of this script (KiB per dispatch), scaled by
+# what the same counters read for a plain 1 GiB device copy (FETCH_SIZE x
+# 2.0, WRITE_SIZE x 1.0; see profiles/).  Keyed by "layer/kernel" of the
+# 70B-block step.  Valid only for the GEMM sources they were taken on (the
+# kernel and the header it includes): reported as null once either changes.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "8eb9791ff195d4a04166db0f7f98cbbb2a90ef00",
-    "fwd_gemm": {"fetch": 2 * 295420.0 * 1024, "write": 147509.0 * 1024},
-    "dgrad_gemm": {"fetch": 2 * 198148.0 * 1024, "write": 32801.0 * 1024},
+    "src_sha1": None,
 }
 
 
-def gemm_traffic(kernel):
+def gemm_traffic(key):
     import hashlib
     h = hashlib.sha1()
     try:
@@ -68,9 +79,9 @@ def gemm_traffic(kernel):
     except OSError:
         return None
     digest = h.hexdigest()
-    if digest != GEMM_TRAFFIC["src_sha1"] or kernel not in GEMM_TRAFFIC:
+    if digest != GEMM_TRAFFIC["src_sha1"] or key not in GEMM_TRAFFIC:
         return None
-    t = GEMM_TRAFFIC[kernel]
+    t = GEMM_TRAFFIC[key]
     return int(t["fetch"] + t["write"])
 
 
@@ -287,18 +298,21 @@ def dropout_passes(Q, x, g, q, A, B, s, h, u, out, ws_f, plain, reps):
             "dropout_term": {"bytes": tb, "GB/s": round(tb / (du * 1e-6) / 1e9, 1) if du else None}}
 
 
-def cpu_baseline(cfg, layer, tokens):
-    """Time the oracle (float64 numpy) on a bounded sample of the workload."""
-    import numpy as np
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return None
 
+
+def cpu_baseline(cfg, layer, tokens):
+    """Time the oracle (float64 numpy) on a bounded sample of the workload:
+    one layer's full quantization, then its forward and backward on a slice
+    of the tokens."""
     import qlora_inputs as QI
     from oracle import qlora_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     L = layer
     inp = QI.layer_inputs(cfg, L, M=tokens)
     t0 = time.perf_counter()
@@ -312,13 +326,149 @@ def cpu_baseline(cfg, layer, tokens):
     O.linear_bwd(x, g, Wd, A, B, L.s, u=u)
     dt = time.perf_counter() - t0
     flops = fwd_flops(tokens, L.n, L.m, L.r) + bwd_flops(tokens, L.n, L.m, L.r)
+    threads = blas_threads()
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(threads) if threads else (os.cpu_count() or 1),
         "kind": "oracle",
-        "sample": (f"quantize the full {L.m}x{L.n} weight + fwd + bwd for {tokens} of the {L.M} tokens, "
-                   f"float64 numpy; {dt:.2f} s; value = sample fwd+bwd flops / time"),
+        "sample": (f"70B block, {L.name} projection {L.m}x{L.n}: quantize the whole weight, dequantize it, then "
+                   f"fwd + bwd for {tokens} of the {L.M} tokens, float64 numpy; {dt:.2f} s; "
+                   f"value = sample fwd+bwd flops / time (quantize and dequantize included)"),
+        "blas_threads": threads,
+        "os_cpu_count": os.cpu_count(),
+        "seconds": round(dt, 2),
+    }
+
+
+GEMM_KERNELS = ("fwd_gemm", "dgrad_gemm")
+KERNELS = ("quantize", "fwd_gemm", "dgrad_gemm", "down_proj", "gpass", "token_grad", "transpose")
+
+
+def gemm_launch_flops(kernel, M, n, m, r):
+    """Algorithmic flops of one GEMM launch: the dense product plus the LoRA
+    term it carries as extra K steps (u B^T or v A)."""
+    if kernel == "fwd_gemm":
+        return 2 * M * m * n + 2 * M * m * r
+    return 2 * M * n * m + 2 * M * n * r
+
+
+class LayerSet:
+    """Device tensors of one workload's layers (drawn on the device), with one
+    forward and one backward workspace shared by all of them."""
+
+    def __init__(self, Q, dev, layers, seed, backward=True):
+        import torch
+        gen = torch.Generator(device=dev).manual_seed(seed)
+        self.Q, self.dev, self.layers = Q, dev, layers
+        self.t = []
+        wf = wb = 256
+        for L in layers:
+            M, n, m, r = L.M, L.n, L.m, L.r
+            W = torch.randn((m, n), generator=gen, device=dev, dtype=torch.float32).mul_(L.w_sigma)
+            d = dict(L=L, W=W, q=Q.alloc_quantized(m, n, dev),
+                     x=torch.randn((M, n), generator=gen, device=dev).to(torch.bfloat16),
+                     A=torch.randn((r, n), generator=gen, device=dev).div_(16).to(torch.bfloat16),
+                     B=torch.randn((m, r), generator=gen, device=dev).mul_(0.01).to(torch.bfloat16),
+                     h=torch.empty((M, m), dtype=torch.bfloat16, device=dev),
+                     u=torch.empty((M, r), dtype=torch.float32, device=dev))
+            if backward:
+                d["g"] = torch.randn((M, m), generator=gen, device=dev).to(torch.bfloat16)
+                d["out"] = (torch.empty((M, n), dtype=torch.bfloat16, device=dev),
+                            torch.empty((r, n), dtype=torch.bfloat16, device=dev),
+                            torch.empty((m, r), dtype=torch.bfloat16, device=dev))
+                wb = max(wb, Q.workspace_bytes(Q.QLORA_OP_BWD, M, n, m, r))
+            wf = max(wf, Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r))
+            self.t.append(d)
+        self.ws_f = torch.empty(wf, dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty(wb, dtype=torch.uint8, device=dev) if backward else None
+        self.quantize()
+
+    def quantize_one(self, d):
+        self.Q.quantize_nf4_dq(d["W"], out=d["q"])
+
+    def fwd_one(self, d):
+        L = d["L"]
+        self.Q.linear_fwd(d["x"], d["q"], d["A"], d["B"], L.s, h=d["h"], u=d["u"], workspace=self.ws_f)
+
+    def bwd_one(self, d):
+        L = d["L"]
+        self.Q.linear_bwd(d["x"], d["g"], d["q"], d["A"], d["B"], L.s, u=d["u"], out=d["out"], workspace=self.ws_b)
+
+    def quantize(self):
+        for d in self.t:
+            self.quantize_one(d)
+
+    def forward(self):
+        for d in self.t:
+            self.fwd_one(d)
+
+    def backward(self):
+        for d in reversed(self.t):
+            self.bwd_one(d)
+
+    def step(self):
+        self.quantize()
+        self.forward()
+        self.backward()
+
+    def flops(self):
+        return sum(fwd_flops(L.M, L.n, L.m, L.r) + bwd_flops(L.M, L.n, L.m, L.r) for L in self.layers)
+
+    def kernel_times(self, reps):
+        """Per layer: average duration of every library kernel over `reps`
+        forward + backward calls of that layer (HIP events on the launch
+        stream), the quantizer's too; checks that no K-split wait ran out."""
+        import torch
+        Q = self.Q
+        out = {}
+        for d in self.t:
+            L = d["L"]
+            Q.profile_enable(True)
+            for _ in range(reps):
+                self.quantize_one(d)
+                self.fwd_one(d)
+                self.bwd_one(d)
+            torch.cuda.synchronize()
+            Q.profile_enable(False)
+            Q.linear_check(Q.QLORA_OP_FWD, L.M, L.n, L.m, L.r, self.ws_f)
+            Q.linear_check(Q.QLORA_OP_BWD, L.M, L.n, L.m, L.r, self.ws_b)
+            kern = {}
+            for name in KERNELS:
+                cnt, tot = Q.profile_query(name)
+                if cnt:
+                    kern[name] = {"launches_per_call": cnt // reps, "us_per_call": round(tot * 1e3 / reps, 2)}
+                    if name in GEMM_KERNELS:
+                        us = tot * 1e3 / cnt
+                        f = gemm_launch_flops(name, L.M, L.n, L.m, L.r)
+                        kern[name].update({"avg_us": round(us, 2), "flop": f,
+                                           "TFLOP/s": round(f / (us * 1e-6) / 1e12, 1),
+                                           "mfma_frac": round(f / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+            out[L.name] = kern
+        return out
+
+
+def layer_passes(ls, reps):
+    """Forward, backward and forward + backward of one layer (median of reps)."""
+    d = ls.t[0]
+    L = d["L"]
+    fwd, _ = timed_us(lambda: ls.fwd_one(d), reps)
+    bwd, _ = timed_us(lambda: ls.bwd_one(d), reps)
+    both, _ = timed_us(lambda: (ls.fwd_one(d), ls.bwd_one(d)), reps)
+    qt, _ = timed_us(lambda: ls.quantize_one(d), reps)
+    ff, bf = fwd_flops(L.M, L.n, L.m, L.r), bwd_flops(L.M, L.n, L.m, L.r)
+    qb = quant_bytes(L.m, L.n)
+    return {
+        "workload": f"{L.name} projection {L.m}x{L.n}, {L.M} tokens, r={L.r}, alpha={L.alpha:g}",
+        "forward": {"us": round(fwd, 2), "TFLOP/s": round(ff / (fwd * 1e-6) / 1e12, 1),
+                    "mfma_frac": round(ff / (fwd * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "backward": {"us": round(bwd, 2), "TFLOP/s": round(bf / (bwd * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(bf / (bwd * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "fwd_bwd": {"us": round(both, 2), "TFLOP/s": round((ff + bf) / (both * 1e-6) / 1e12, 1),
+                    "mfma_frac": round((ff + bf) / (both * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "quantize": {"us": round(qt, 2), "GB/s": round(qb / (qt * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(qb / (qt * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "timing": "back-to-back, no cache flush"},
     }
 
 
@@ -327,7 +477,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--profile-reps", type=int, default=3, help="per-layer calls timed kernel by kernel")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the measurements outside the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,7 +489,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import bit_quantized_fine_qlora_amd as Q
@@ -358,76 +508,35 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
 
-    cfg = 2
-    L = QI.WORKLOADS[cfg]["layers"][0]
-    M, n, m, r, s = L.M, L.n, L.m, L.r, L.s
-    inp = QI.layer_inputs(cfg, L)
-
-    def dev_bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    W = torch.from_numpy(inp["W"]).to(dev)
-    x, g, A, B = (dev_bf16(inp[k]) for k in ("x", "g", "A", "B"))
-    q = Q.alloc_quantized(m, n, dev)
-    h = torch.empty((M, m), dtype=torch.bfloat16, device=dev)
-    u = torch.empty((M, r), dtype=torch.float32, device=dev)
-    gx = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
-    gA = torch.empty((r, n), dtype=torch.bfloat16, device=dev)
-    gB = torch.empty((m, r), dtype=torch.bfloat16, device=dev)
-    ws_f = torch.empty(Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(Q.workspace_bytes(Q.QLORA_OP_BWD, M, n, m, r), dtype=torch.uint8, device=dev)
-
-    def step():
-        Q.quantize_nf4_dq(W, out=q)
-        Q.linear_fwd(x, q, A, B, s, h=h, u=u, workspace=ws_f)
-        Q.linear_bwd(x, g, q, A, B, s, u=u, out=(gx, gA, gB), workspace=ws_b)
-
+    cfg = 5
+    blk = LayerSet(Q, dev, QI.WORKLOADS[cfg]["layers"], seed=cfg)
+    M, r, s = blk.layers[0].M, blk.layers[0].r, blk.layers[0].s
     for _ in range(args.warmup):
-        step()
+        blk.step()
     torch.cuda.synchronize()
+    print(f"[bench] 70B block: {args.warmup} warm-up steps done", file=sys.stderr, flush=True)
 
-    Q.profile_enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        blk.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    Q.profile_enable(False)
-
     ms = (t1 - t0) * 1e3 / args.steps
-    flops = fwd_flops(M, n, m, r) + bwd_flops(M, n, m, r)
+    flops = blk.flops()
     value = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] 70B block: {args.steps} timed steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    kern = {}
-    for name in ("quantize", "fwd_gemm", "dgrad_gemm", "down_proj", "gpass", "token_grad", "transpose"):
-        cnt, tot = Q.profile_query(name)
-        if cnt:
-            kern[name] = {"launches": cnt, "avg_us": tot * 1e3 / cnt}
-
-    per_launch = {
-        "fwd_gemm": 2 * M * m * n + 2 * M * m * r,
-        "dgrad_gemm": 2 * M * n * m + 2 * M * n * r,
-    }
-    dom = max(per_launch, key=lambda k: kern.get(k, {}).get("avg_us", 0.0))
-    dom_us = kern[dom]["avg_us"]
-    achieved = per_launch[dom] / (dom_us * 1e-6) / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic(dom)}
-    qb = quant_bytes(m, n)
-    quant = {"avg_us": round(kern["quantize"]["avg_us"], 2),
-             "GB/s": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9, 1),
-             "hbm_frac": round(qb / (kern["quantize"]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    other = {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()}
-
-    extra = {}
-    if not args.no_extra:
-        fwd_med, _ = timed_us(lambda: Q.linear_fwd(x, q, A, B, s, h=h, u=u, workspace=ws_f), 10)
-        bwd_med, _ = timed_us(lambda: Q.linear_bwd(x, g, q, A, B, s, u=u, out=(gx, gA, gB), workspace=ws_b), 10)
-        extra["passes"] = {
-            "forward": {"us": round(fwd_med, 2), "TFLOP/s": round(fwd_flops(M, n, m, r) / (fwd_med * 1e-6) / 1e12, 1)},
-            "backward": {"us": round(bwd_med, 2), "TFLOP/s": round(bwd_flops(M, n, m, r) / (bwd_med * 1e-6) / 1e12, 1)},
-        }
+    # per-layer kernel times (a separate pass with the library's HIP events)
+    layers = blk.kernel_times(args.profile_reps)
+    gemms = [(f"{nm}/{k}", v) for nm, kk in layers.items() for k, v in kk.items() if k in GEMM_KERNELS]
+    dom_key, dom = max(gemms, key=lambda kv: kv[1]["avg_us"])
+    achieved = dom["flop"] / (dom["avg_us"] * 1e-6) / 1e12
+    roofline = {"kernel": dom_key, "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic(dom_key),
+                "per_launch_flop": dom["flop"], "avg_us": dom["avg_us"]}
+    gemm_flop = sum(v["flop"] * v["launches_per_call"] for _, v in gemms)
+    gemm_us = sum(v["us_per_call"] for _, v in gemms)
+    print(f"[bench] per-layer kernel times done", file=sys.stderr, flush=True)
 
     out = {
         "metric": "QLoRA linear fwd+bwd TFLOP/s and NF4 weight GB/s (% of roofline), 1 MI355X",
@@ -442,25 +551,63 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gate projection W0 14336x4096 NF4+DQ, 4096 tokens, r=16, alpha=32: "
-                               "quantize + fwd + bwd per step",
-                   "M": M, "n": n, "m": m, "r": r, "s": s},
+        "config": {"workload": "70B-shaped block (q 8192x8192, k/v 1024x8192, o 8192x8192, gate/up 28672x8192, "
+                               "down 8192x28672) NF4+DQ, 8192 tokens, r=64, alpha=16 on all seven: quantize + "
+                               "fwd + bwd of the seven layers per step",
+                   "M": M, "r": r, "s": s, "layers": len(blk.layers), "step_flop": flops},
         "roofline": roofline,
-        "quantize": quant,
-        "kernels": other,
+        "block_gemms": {"flop": gemm_flop, "us": round(gemm_us, 1),
+                        "TFLOP/s": round(gemm_flop / (gemm_us * 1e-6) / 1e12, 1),
+                        "mfma_frac": round(gemm_flop / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "note": "all 14 GEMM launches of a step, summed from the per-layer kernel times"},
+        "layers": layers,
     }
-    out.update(extra)
     if not args.no_extra:
-        out["dropout"] = dropout_passes(Q, x, g, q, A, B, s, h, u, (gx, gA, gB), ws_f, extra["passes"], 10)
-        out["adapter_merge"] = adapter_merge(Q, q, A, B, s, 10)
+        fwd, _ = timed_us(blk.forward, 5)
+        bwd, _ = timed_us(blk.backward, 5)
+        ff = sum(fwd_flops(L.M, L.n, L.m, L.r) for L in blk.layers)
+        bf = sum(bwd_flops(L.M, L.n, L.m, L.r) for L in blk.layers)
+        qb = sum(quant_bytes(L.m, L.n) for L in blk.layers)
+        qt, qmin = timed_us(blk.quantize, 5)
+        out["block_passes"] = {
+            "forward": {"us": round(fwd, 1), "TFLOP/s": round(ff / (fwd * 1e-6) / 1e12, 1)},
+            "backward": {"us": round(bwd, 1), "TFLOP/s": round(bf / (bwd * 1e-6) / 1e12, 1)},
+            "fwd_bwd_without_quantize_us": round(fwd + bwd, 1),
+            "fwd_bwd_without_quantize_TFLOP/s": round((ff + bf) / ((fwd + bwd) * 1e-6) / 1e12, 1),
+            "quantize": {"us": round(qt, 1), "bytes": qb, "GB/s": round(qb / (qt * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(qb / (qt * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "the seven fp32 weights (3.42 GB, larger than the caches), back to back"},
+        }
+        print(f"[bench] block passes done", file=sys.stderr, flush=True)
+    del blk
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        gate = LayerSet(Q, dev, QI.WORKLOADS[2]["layers"], seed=2)
+        out["gate_8B"] = layer_passes(gate, 10)
+        d = gate.t[0]
+        L = d["L"]
+        out["gate_8B"]["kernels"] = gate.kernel_times(5)[L.name]
+        out["dropout"] = dropout_passes(Q, d["x"], d["g"], d["q"], d["A"], d["B"], L.s, d["h"], d["u"], d["out"],
+                                        gate.ws_f, out["gate_8B"], 10)
+        out["adapter_merge"] = adapter_merge(Q, d["q"], d["A"], d["B"], L.s, 10)
+        out["level_tables"] = level_table_variants(Q, d["W"], d["q"], 10)
+        del gate, d
+        torch.cuda.empty_cache()
+        print(f"[bench] gate projection done", file=sys.stderr, flush=True)
+        down = LayerSet(Q, dev, QI.WORKLOADS[3]["layers"], seed=3)
+        out["down_8B"] = layer_passes(down, 10)
+        out["down_8B"]["kernels"] = down.kernel_times(5)[down.layers[0].name]
+        del down
+        torch.cuda.empty_cache()
+        print(f"[bench] down projection done", file=sys.stderr, flush=True)
         out["adapter_adam"] = adapter_adam(Q, dev, 10)
-        out["level_tables"] = level_table_variants(Q, W, q, 10)
-        del W, x, g, A, B, h, gx, ws_f, ws_b
         torch.cuda.empty_cache()
         out["small_tokens"] = small_token_block(Q, dev, 10)
+        print(f"[bench] extras done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, QI.WORKLOADS[cfg]["layers"][0], args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -19,6 +19,7 @@ from .api import (  # noqa: F401
     dequant_dq,
     dequant_nf4_dq,
     linear_bwd,
+    linear_check,
     linear_fwd,
     linear_fwd_grouped,
     merge_adapter,

@@ -63,6 +63,7 @@ PROTOTYPES = {
     "qlora_linear_bwd_ex": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(Dropout), c_vp, c_sz,
                                            c_vp]),
+    "qlora_linear_check": (ctypes.c_int, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp]),
     "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "qlora_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
 }

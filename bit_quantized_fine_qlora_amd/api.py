@@ -315,6 +315,13 @@ def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Te
     return gx, gA, gB
 
 
+def linear_check(op: int, M: int, n: int, m: int, r: int, workspace: torch.Tensor) -> None:
+    """Raise if the last call of `op` on `workspace` had a bounded wait run out
+    (qlora_linear_check; synchronizes the current stream)."""
+    st = _lib.load().qlora_linear_check(int(op), M, n, m, r, _ptr(workspace), _stream(workspace.device))
+    _lib.check(st, "qlora_linear_check")
+
+
 def profile_enable(on: bool = True) -> None:
     _lib.check(_lib.load().qlora_profile_enable(1 if on else 0), "qlora_profile_enable")
 

@@ -22,6 +22,7 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
                      float s, void* split_ws, const Nf4Table& tab, hipStream_t stream);
 size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K);
+int64_t gemm_giveup_offset(int64_t M, int64_t N, int64_t K);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream,
@@ -330,6 +331,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace is NULL or too small";
     case QLORA_ERR_HIP: return "a HIP launch failed";
     case QLORA_ERR_VALUE: return "invalid value (non-finite s or unknown op)";
+    case QLORA_ERR_INCOMPLETE: return "a bounded wait inside a kernel ran out: that call's outputs are unreliable";
     default: return "unknown status";
   }
 }
@@ -660,6 +662,34 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     }
   }
   return hip_status();
+}
+
+qlora_status qlora_linear_check(int op, int64_t M, int64_t n, int64_t m, int32_t r, const void* workspace,
+                                qlora_stream_t stream) {
+  qlora_status st = check_linear(M, n, m, r, 1.0f);
+  if (st != QLORA_OK) return st;
+  if (op != QLORA_OP_FWD && op != QLORA_OP_BWD && op != QLORA_OP_BWD_DROPOUT) return QLORA_ERR_VALUE;
+  int64_t off = -1;
+  if (op == QLORA_OP_FWD) {
+    if (M > small_max_tokens()) {
+      const FwdWs w = fwd_ws(M, n, m, r);
+      const int64_t g = gemm_giveup_offset(M, m, n);
+      if (w.has_ksplit && g >= 0) off = (int64_t)w.ksplit + g;
+    }
+  } else {
+    const BwdWs w = bwd_ws(M, n, m, r, op == QLORA_OP_BWD_DROPOUT);
+    const int64_t g = gemm_giveup_offset(M, n, w.m_pad);
+    if (w.has_ksplit && g >= 0) off = (int64_t)w.ksplit + g;
+  }
+  if (off < 0) return QLORA_OK;  // this call has no bounded wait
+  if (!workspace) return QLORA_ERR_NULL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, static_cast<const uint8_t*>(workspace) + off, sizeof(word), hipMemcpyDeviceToHost, hs) !=
+          hipSuccess ||
+      hipStreamSynchronize(hs) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return word ? QLORA_ERR_INCOMPLETE : QLORA_OK;
 }
 
 qlora_status qlora_profile_enable(int on) {

@@ -95,7 +95,8 @@ struct GemmArgs {
   int full_tiles;
   int nsplit;
   float* partial;         // nsplit x 256 x 256 fp32, the first finisher's sum
-  uint32_t* split_sync;   // nsplit x {arrivals, partial ready}, zero at launch
+  uint32_t* split_sync;   // nsplit x {arrivals, partial ready}, then the
+                          // give-up word; all zero at launch
   const float* add;       // M x N fp32 added before the rounding, or null
   // Few tiles (see gemm_pieces): pieces > 1 runs every tile as that many K
   // pieces, work item b being piece b % pieces of tile b / pieces; each piece
@@ -479,10 +480,19 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
       if (tid == 0) __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
+    bool ready = false;
     for (uint32_t it = 0; it < kSplitSpinLimit; ++it) {
-      if (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        ready = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(2);
     }
+    // A wait that runs out leaves the tile without the other half's sum:
+    // the give-up word after the hand-off words records it for the host
+    // (qlora_linear_check), instead of the tile being wrong silently.
+    if (!ready && tid == 0)
+      __hip_atomic_store(p.split_sync + 2 * p.nsplit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     part_bytes = lg2::BF * lg2::BT * 4;
   }
   {
@@ -703,7 +713,16 @@ size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K) {
   if (pc > 1) return (size_t)pc * tiles_of(M, N) * lg2::BF * lg2::BT * sizeof(float);
   const size_t ns = (size_t)gemm_split_tiles(M, N, K);
   if (!ns) return 0;
-  return ns * lg2::BF * lg2::BT * sizeof(float) + ((2 * ns * sizeof(uint32_t) + 255) / 256) * 256;
+  return ns * lg2::BF * lg2::BT * sizeof(float) + (((2 * ns + 1) * sizeof(uint32_t) + 255) / 256) * 256;
+}
+
+// Byte offset, inside the split workspace, of the give-up word of a GEMM
+// whose last round is split in K, or -1 when the GEMM has no hand-off.
+int64_t gemm_giveup_offset(int64_t M, int64_t N, int64_t K) {
+  if (gemm_pieces(M, N, K) > 1) return -1;
+  const int64_t ns = gemm_split_tiles(M, N, K);
+  if (!ns) return -1;
+  return ns * lg2::BF * lg2::BT * (int64_t)sizeof(float) + 2 * ns * (int64_t)sizeof(uint32_t);
 }
 
 // split_ws: gemm_split_ws_bytes(M, N, K) bytes (16-byte aligned), or null to
@@ -742,7 +761,8 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
     p.partial = static_cast<float*>(split_ws);
     p.split_sync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(split_ws) +
                                                (size_t)ns * lg2::BF * lg2::BT * sizeof(float));
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((2 * ns + 255) / 256), dim3(256), 0, stream, p.split_sync, 2 * ns);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((2 * ns + 1 + 255) / 256), dim3(256), 0, stream, p.split_sync,
+                       2 * ns + 1);
   }
   const int grid = tiles + ns;
   if (bwd)

@@ -46,7 +46,8 @@ typedef enum {
   QLORA_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
   QLORA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
   QLORA_ERR_HIP = -6,       /* a HIP launch or query failed */
-  QLORA_ERR_VALUE = -7      /* s is not finite, or an unknown op id */
+  QLORA_ERR_VALUE = -7,     /* s is not finite, or an unknown op id */
+  QLORA_ERR_INCOMPLETE = -8 /* a kernel's bounded wait ran out (qlora_linear_check) */
 } qlora_status;
 
 /* Human-readable text of a status code (static storage). */
@@ -340,6 +341,23 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
                                  qlora_bf16* grad_x, qlora_bf16* grad_A, qlora_bf16* grad_B,
                                  const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
                                  qlora_stream_t stream);
+
+/*
+ * Completion check of the last qlora_linear_fwd / qlora_linear_bwd(_ex)
+ * call (op QLORA_OP_FWD, QLORA_OP_BWD or QLORA_OP_BWD_DROPOUT) that used
+ * `workspace` with these sizes.  When a GEMM has more output tiles than the
+ * GPU has compute units and its last round is at most half full, the tiles
+ * of that round run as two K halves: the half that finishes second waits,
+ * for a bounded time, for the other half's fp32 sum ("QLoRA: Efficient
+ * Fine-Tuning", Step 3, Eq. 3: the output those tiles hold).  If that wait
+ * ever ran out, the call wrote a give-up word in its workspace and this
+ * returns QLORA_ERR_INCOMPLETE (that call's h or grad_x is then unreliable);
+ * QLORA_OK otherwise, and always for calls without such a split.  The word
+ * is cleared by the next call that uses the workspace.  Synchronizes
+ * `stream` (it reads one word back to the host).
+ */
+qlora_status qlora_linear_check(int op, int64_t M, int64_t n, int64_t m, int32_t r, const void* workspace,
+                                qlora_stream_t stream);
 
 /*
  * Kernel timing (tracing aid, off by default).  While enabled, every kernel

@@ -63,7 +63,7 @@ def test_level_tables_match_oracle(lib):
 
 
 def test_status_strings(lib):
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert len(lib.qlora_status_string(st)) >= 2
     assert lib.qlora_version() >= 100
 
@@ -152,6 +152,20 @@ def test_workspace_sizes(lib):
     assert lib.qlora_workspace_bytes(0, 32, 100, 256, 8) == 0
     assert lib.qlora_workspace_bytes(7, 32, 256, 256, 8) == 0
     assert lib.qlora_workspace_bytes(0, 32, 256, 256, 0) == 0
+
+
+def test_linear_check_without_hand_off(lib):
+    # calls that have no bounded wait are complete by construction: OK with
+    # nothing read back (no GPU is touched); bad arguments are rejected first
+    f = lib.qlora_linear_check
+    assert f(0, 16, 4096, 1024, 16, None, None) == 0       # weight-streaming forward
+    assert f(0, 4096, 4096, 4096, 16, None, None) == 0     # 256 tiles: one full round
+    assert f(1, 256, 4096, 14336, 16, None, None) == 0     # few tiles: K pieces, no wait
+    assert f(3, 4096, 4096, 4096, 16, None, None) == -7    # unknown op
+    assert f(0, 4096, 100, 4096, 16, None, None) == -2     # n % 64 != 0
+    assert f(0, 4096, 4096, 4096, 0, None, None) == -3     # r = 0
+    # the gate projection's forward splits its last round: the workspace is needed
+    assert f(0, 4096, 4096, 14336, 16, None, None) == -1
 
 
 def layer_desc(n=256, m=256, r=8, s=2.0, x=1 << 20, h=1 << 20, u=0):

@@ -154,9 +154,12 @@ def test_k_split_last_round(Q, M, n, m, r, s):
     got, _ = check_full(Q, inp["W"], inp, s, need_bwd=False, label=f"k-split M={M} n={n} m={m} r={r}")
     say("k-split determinism")
     x, A, B = dev_bf16(inp["x"]), dev_bf16(inp["A"]), dev_bf16(inp["B"])
+    ws = torch.empty(Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r), dtype=torch.uint8, device="cuda")
     for _ in range(2):
-        h2, u2 = Q.linear_fwd(x, got["q"], A, B, s)
+        h2, u2 = Q.linear_fwd(x, got["q"], A, B, s, workspace=ws)
         torch.cuda.synchronize()
+        # no hand-off wait ran out (the give-up word stayed zero)
+        Q.linear_check(Q.QLORA_OP_FWD, M, n, m, r, ws)
         assert torch.equal(h2, got["h"]) and torch.equal(u2, got["u"])
 
 
@@ -173,11 +176,34 @@ FEW_TILES = [
 ]
 
 
+def expected_pieces(M, N, K, cus):
+    """K pieces per output tile of the few-tile mode: P = min(CUs / tiles, 16)
+    when the tiles fill at most half the CUs, lowered until every piece keeps
+    at least 8 K steps of 64."""
+    tiles = -(-M // 256) * -(-N // 256)
+    if tiles * 2 > cus:
+        return 1, tiles
+    pc = min(cus // tiles, 16)
+    nk = -(-K // 64)
+    while pc > 1 and nk // pc < 8:
+        pc -= 1
+    return pc, tiles
+
+
 @pytest.mark.parametrize("M,n,m,r,s", FEW_TILES)
 def test_k_pieces_few_tiles(Q, M, n, m, r, s):
     lib = Q._lib.load()
-    tiles = -(-M // 256) * -(-m // 256)
-    assert lib.qlora_workspace_bytes(0, M, n, m, r) >= 2 * M * m * 4 or tiles * 2 > 256, "K-piece planes not in the workspace"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pf, tf = expected_pieces(M, m, n, cus)      # forward: N = m, K = n
+    pb, tb = expected_pieces(M, n, m, cus)      # grad_x: N = n, K = m
+    if pf == 1 and pb == 1:
+        pytest.skip(f"{tf} / {tb} tiles on {cus} CUs: neither GEMM runs in K pieces")
+    # each GEMM that runs in pieces keeps P fp32 planes of 256 x 256 per tile in its workspace
+    if pf > 1:
+        assert lib.qlora_workspace_bytes(0, M, n, m, r) >= pf * tf * 256 * 256 * 4, "forward K-piece planes missing"
+    if pb > 1:
+        assert lib.qlora_workspace_bytes(1, M, n, m, r) >= pb * tb * 256 * 256 * 4, "grad_x K-piece planes missing"
+    say(f"k-pieces: forward P={pf} ({tf} tiles), grad_x P={pb} ({tb} tiles)")
     inp = QI.custom_inputs(seed=7 * M + m + 11 * r, M=M, n=n, m=m, r=r)
     got, _ = check_full(Q, inp["W"], inp, s, label=f"k-pieces M={M} n={n} m={m} r={r}")
     say("k-pieces determinism")
