@@ -21,6 +21,7 @@ from .api import (  # noqa: F401
     linear_bwd,
     linear_check,
     linear_fwd,
+    linear_fwd_static,
     linear_fwd_grouped,
     merge_adapter,
     level_table,

@@ -54,6 +54,8 @@ PROTOTYPES = {
     "qlora_workspace_bytes": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32]),
     "qlora_linear_fwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qlora_linear_fwd_static": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                               c_vp, c_vp, c_vp, c_vp]),
     "qlora_grouped_workspace_bytes": (c_sz, [c_i64, c_i32, ctypes.POINTER(LinearLayer)]),
     "qlora_linear_fwd_grouped": (ctypes.c_int, [c_i64, c_i32, ctypes.POINTER(LinearLayer), c_vp, c_sz, c_vp]),
     "qlora_linear_bwd": (ctypes.c_int, [c_i64, c_i64, c_i64, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

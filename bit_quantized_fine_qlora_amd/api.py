@@ -226,6 +226,25 @@ def linear_fwd(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Te
     return h, u
 
 
+def linear_fwd_static(x: torch.Tensor, q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, s: float,
+                      h: torch.Tensor, u: torch.Tensor | None = None):
+    """qlora_linear_fwd_static: the forward with the library's own device scratch
+    (no workspace).  h (and u, if wanted) must be given: nothing is allocated."""
+    M, n = x.shape
+    m = q.m
+    r = A.shape[0]
+    _need(x, torch.bfloat16, (M, q.n), "x")
+    _need(A, torch.bfloat16, (r, q.n), "A")
+    _need(B, torch.bfloat16, (m, r), "B")
+    _need(h, torch.bfloat16, (M, m), "h")
+    if u is not None:
+        _need(u, torch.float32, (M, r), "u")
+    st = _lib.load().qlora_linear_fwd_static(M, n, m, r, float(s), _ptr(x), _ptr(q.codes), _ptr(q.absmax8),
+                                             _ptr(q.c2), _ptr(A), _ptr(B), _ptr(h), _ptr(u), _stream(x.device))
+    _lib.check(st, "qlora_linear_fwd_static")
+    return h, u
+
+
 class GroupedForward:
     """A reusable grouped forward: outputs, descriptors and workspace are made once.
 
@@ -315,10 +334,12 @@ def linear_bwd(x: torch.Tensor, g: torch.Tensor, q: QuantizedWeight, A: torch.Te
     return gx, gA, gB
 
 
-def linear_check(op: int, M: int, n: int, m: int, r: int, workspace: torch.Tensor) -> None:
+def linear_check(op: int, M: int, n: int, m: int, r: int, workspace: torch.Tensor | None) -> None:
     """Raise if the last call of `op` on `workspace` had a bounded wait run out
-    (qlora_linear_check; synchronizes the current stream)."""
-    st = _lib.load().qlora_linear_check(int(op), M, n, m, r, _ptr(workspace), _stream(workspace.device))
+    (qlora_linear_check; synchronizes the current stream).  workspace None with
+    the forward op: the scratch of linear_fwd_static."""
+    dev = workspace.device if workspace is not None else None
+    st = _lib.load().qlora_linear_check(int(op), M, n, m, r, _ptr(workspace), _stream(dev))
     _lib.check(st, "qlora_linear_check")
 
 

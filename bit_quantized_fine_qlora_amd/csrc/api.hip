@@ -11,6 +11,14 @@
 #include "../../include/qlora.h"
 #include "qlora_common.h"
 
+// Scratch of qlora_linear_fwd_static, one copy per device (see static_scratch
+// below): 64 MiB, enough for the forward's split partials, u and the GEMM's
+// K-split sums at every shape whose workspace fits; larger layouts drop the
+// K split or are refused.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static_assert(kStaticScratchBytes == QLORA_STATIC_SCRATCH_BYTES, "scratch size differs from the header");
+
 namespace qlora {
 
 // kernels (defined in the other translation units)
@@ -309,6 +317,33 @@ qlora_status make_dropout(const qlora_dropout* d, DropoutDev& out, float& inv_ke
   return QLORA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch of qlora_linear_fwd_static (callers that cannot
+// allocate device memory).  Each device the library runs on holds its own
+// copy of this array until the process ends.  In host code `scratch` only
+// names the array: its device address comes from hipGetSymbolAddress, once
+// per device (with that device current), and only that address is ever
+// handed to kernels.  Every call on a device shares its array: calls that
+// overlap on one device race.  The K-split counters that must start at zero
+// are cleared by a fill kernel in the stream before each GEMM that uses them.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+qlora_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return QLORA_OK;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(base) + off);
@@ -472,25 +507,25 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
                              workspace_bytes, stream);
 }
 
-qlora_status qlora_linear_fwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
-                                 const uint8_t* codes, const uint8_t* absmax8, const float* c2,
-                                 const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
-                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
-                                 qlora_stream_t stream) {
+// Checks shared by the forward entry points (everything but the workspace).
+static qlora_status check_fwd_args(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                   const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                   const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out) {
   qlora_status st = check_linear(M, n, m, r, s);
-  if (st != QLORA_OK) return st;
-  DropoutDev dd;
-  float inv_keep;
-  st = make_dropout(dropout, dd, inv_keep);
   if (st != QLORA_OK) return st;
   if (!x || !codes || !absmax8 || !c2 || !A || !B || !h) return QLORA_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax8) || !aligned16(c2) || !aligned16(A) ||
       !aligned16(B) || !aligned16(h) || (u_out && !aligned16(u_out)))
     return QLORA_ERR_ALIGN;
-  const FwdWs w = fwd_ws(M, n, m, r);
-  if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  return QLORA_OK;
+}
+
+// The forward's launches on a checked workspace laid out by fwd_ws; with
+// use_ksplit false the GEMM runs every tile whole (no K-split region needed).
+static qlora_status run_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                            const uint8_t* codes, const uint8_t* absmax8, const float* c2, const qlora_bf16* A,
+                            const qlora_bf16* B, qlora_bf16* h, float* u_out, const DropoutDev& dd, float inv_keep,
+                            const FwdWs& w, bool use_ksplit, void* workspace, hipStream_t hs) {
   if (M <= small_max_tokens()) {
     SmallLayerHost L{x, codes, absmax8, c2, A, B, h, u_out, n, m, r, s, workspace};
     L.drop = dd;
@@ -507,9 +542,51 @@ qlora_status qlora_linear_fwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
   {
     Timed tm("fwd_gemm", hs);
     launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s,
-                    w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs);
+                    (use_ksplit && w.has_ksplit) ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs);
   }
   return hip_status();
+}
+
+qlora_status qlora_linear_fwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                 const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                 const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
+                                 const qlora_dropout* dropout, void* workspace, size_t workspace_bytes,
+                                 qlora_stream_t stream) {
+  qlora_status st = check_fwd_args(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out);
+  if (st != QLORA_OK) return st;
+  DropoutDev dd;
+  float inv_keep;
+  st = make_dropout(dropout, dd, inv_keep);
+  if (st != QLORA_OK) return st;
+  const FwdWs w = fwd_ws(M, n, m, r);
+  if (!workspace || workspace_bytes < w.total) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+  return run_fwd(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out, dd, inv_keep, w, true, workspace,
+                 reinterpret_cast<hipStream_t>(stream));
+}
+
+qlora_status qlora_linear_fwd_static(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                     const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                     const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
+                                     qlora_stream_t stream) {
+  qlora_status st = check_fwd_args(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out);
+  if (st != QLORA_OK) return st;
+  const FwdWs w = fwd_ws(M, n, m, r);
+  // The whole layout if it fits; otherwise the layout without the GEMM's
+  // K-split region (it sits last), whose tiles then run whole.
+  bool use_ksplit = true;
+  if (w.total > kStaticScratchBytes) {
+    use_ksplit = false;
+    if (!w.has_ksplit || w.ksplit > kStaticScratchBytes) return QLORA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != QLORA_OK) return st;
+  DropoutDev dd;
+  float inv_keep;
+  make_dropout(nullptr, dd, inv_keep);
+  return run_fwd(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out, dd, inv_keep, w, use_ksplit, ws,
+                 reinterpret_cast<hipStream_t>(stream));
 }
 
 static qlora_status check_layer(int64_t M, const qlora_linear_layer& L) {
@@ -682,6 +759,14 @@ qlora_status qlora_linear_check(int op, int64_t M, int64_t n, int64_t m, int32_t
     if (w.has_ksplit && g >= 0) off = (int64_t)w.ksplit + g;
   }
   if (off < 0) return QLORA_OK;  // this call has no bounded wait
+  if (!workspace && op == QLORA_OP_FWD) {
+    // qlora_linear_fwd_static's scratch, when its layout kept the K split
+    if (fwd_ws(M, n, m, r).total > kStaticScratchBytes) return QLORA_OK;
+    void* ws = nullptr;
+    const qlora_status st2 = static_scratch(&ws);
+    if (st2 != QLORA_OK) return st2;
+    workspace = ws;
+  }
   if (!workspace) return QLORA_ERR_NULL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   uint32_t word = 0;

@@ -233,6 +233,29 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
                               size_t workspace_bytes, qlora_stream_t stream);
 
 /*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  Same arguments, results and rules as
+ * qlora_linear_fwd (with a workspace of qlora_workspace_bytes(0, ...) the
+ * two give identical bits).  The scratch is a library-owned device array of
+ * QLORA_STATIC_SCRATCH_BYTES per device, held until the process ends; the
+ * call allocates and frees nothing.  When the forward's workspace layout is
+ * larger than that array, the call runs its GEMM without the K-split region
+ * (every output tile whole: same results up to fp32 summation order) if the
+ * rest fits, and otherwise returns QLORA_ERR_WORKSPACE before launching
+ * anything.  Every call on a device shares that device's array, which keeps
+ * the last call's contents: calls that overlap on one device (several
+ * streams or threads without ordering) race and must not be issued.
+ * qlora_linear_check(QLORA_OP_FWD, ..., NULL, stream) checks the last such
+ * call.
+ */
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+qlora_status qlora_linear_fwd_static(int64_t M, int64_t n, int64_t m, int32_t r, float s, const qlora_bf16* x,
+                                     const uint8_t* codes, const uint8_t* absmax8, const float* c2,
+                                     const qlora_bf16* A, const qlora_bf16* B, qlora_bf16* h, float* u_out,
+                                     qlora_stream_t stream);
+
+/*
  * One layer of a grouped forward: the arguments of qlora_linear_fwd for one
  * weight (all device pointers, same rules).  Host struct.
  */
@@ -353,8 +376,10 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
  * ever ran out, the call wrote a give-up word in its workspace and this
  * returns QLORA_ERR_INCOMPLETE (that call's h or grad_x is then unreliable);
  * QLORA_OK otherwise, and always for calls without such a split.  The word
- * is cleared by the next call that uses the workspace.  Synchronizes
- * `stream` (it reads one word back to the host).
+ * is cleared by the next call that uses the workspace.  With op
+ * QLORA_OP_FWD, a NULL workspace means the library's scratch of
+ * qlora_linear_fwd_static.  Synchronizes `stream` (it reads one word back
+ * to the host).
  */
 qlora_status qlora_linear_check(int op, int64_t M, int64_t n, int64_t m, int32_t r, const void* workspace,
                                 qlora_stream_t stream);

@@ -164,8 +164,21 @@ def test_linear_check_without_hand_off(lib):
     assert f(3, 4096, 4096, 4096, 16, None, None) == -7    # unknown op
     assert f(0, 4096, 100, 4096, 16, None, None) == -2     # n % 64 != 0
     assert f(0, 4096, 4096, 4096, 0, None, None) == -3     # r = 0
-    # the gate projection's forward splits its last round: the workspace is needed
-    assert f(0, 4096, 4096, 14336, 16, None, None) == -1
+    # this grad_x GEMM (896 tiles) splits its last round: the workspace is needed
+    assert f(1, 4096, 14336, 4096, 16, None, None) == -1
+
+
+def test_static_forward_rejects_large_layouts(lib):
+    # u and the split partials of 262144 tokens at r = 128 need far more than
+    # the 64 MiB scratch: refused before anything touches the GPU
+    f = lib.qlora_linear_fwd_static
+    assert lib.qlora_workspace_bytes(0, 262144, 64, 64, 128) > 64 << 20
+    assert f(262144, 64, 64, 128, 1.0, P, P, P, P, P, P, P, None, None) == -5
+    # argument errors come first, as for qlora_linear_fwd
+    assert f(16, 100, 64, 8, 1.0, P, P, P, P, P, P, P, None, None) == -2
+    assert f(16, 64, 64, 8, 1.0, None, P, P, P, P, P, P, None, None) == -1
+    assert f(16, 64, 64, 8, 1.0, MIS, P, P, P, P, P, P, None, None) == -4
+    assert f(16, 64, 64, 0, 1.0, P, P, P, P, P, P, P, None, None) == -3
 
 
 def layer_desc(n=256, m=256, r=8, s=2.0, x=1 << 20, h=1 << 20, u=0):
