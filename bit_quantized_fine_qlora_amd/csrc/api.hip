@@ -53,7 +53,8 @@ void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y
 int token_grad_splits(int64_t M, int64_t J, int R);
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
                        int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop);
+                       const DropoutDev* drop, uint16_t* planes);
+size_t token_planes_bytes(int64_t M, int R);
 void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
                               const DropoutDev& drop, float* out, hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
@@ -260,7 +261,7 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, ksplit, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, planes, ksplit, total;
   int su, sv, sa, sb;
   bool gpass;     // v and grad_B from one read of g
   bool has_ksplit;
@@ -291,6 +292,8 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
   // dropout: the masked adapter part of grad_x in fp32
   w.dterm = dropout ? L.take((size_t)M * n * sizeof(float)) : 0;
+  // bf16 hi / lo planes of u (grad_B) and then of v (grad_A)
+  w.planes = L.take(token_planes_bytes(M, r));
   // grad_x GEMM tiles split in K (few tiles, or a short last round)
   const size_t kb = gemm_split_ws_bytes(M, n, w.m_pad);
   w.ksplit = kb ? L.take(kb) : 0;
@@ -712,13 +715,15 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     }
     {
       Timed tm("token_grad", hs);
-      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr);
+      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr,
+                        at<uint16_t>(workspace, w.planes));
     }
   }
   {
     Timed tm("token_grad", hs);
     // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p)
-    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd);
+    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd,
+                      at<uint16_t>(workspace, w.planes));
   }
   if (grad_x) {
     if (drop) {

@@ -627,7 +627,8 @@ __global__ void zero_u32_kernel(uint32_t* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-static int device_cus() {
+// Compute units of the current device (256 when no device answers).
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -614,62 +614,424 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// Streaming adapter products for many tokens (the masked calls of LoRA
+// dropout keep the kernels above, which apply the mask between load and
+// LDS store):
+//   skinny_down_kernel : part[split][t][q] = sum_{k in split} X[t][k] Y[q][k]
+//   skinny_token_kernel: part[split][j][q] = sum_{t in split} X[t][j] P[q][t]
+// X streams through an NS-stage LDS ring filled by direct-to-LDS buffer loads
+// (no registers in between, no LDS store instructions), the small operand
+// rides along the same way in bf16: A or B^T for the down products; for the
+// token products the fp32 factor (u or v) as bf16 hi and lo planes [q][t],
+// written once per call by split_planes_kernel.  Each stage is a separate
+// LDS array and every loop over the ring is unrolled by NS, so the compiler
+// sees which stage each fragment read touches and does not make it wait for
+// the loads in flight into the other stages.  A wave waits only for its own
+// loads of the stage it is about to read (loads complete in order), then
+// one barrier publishes the stage and frees the oldest one for the next
+// loads.  Rows, columns and k past the split or the tensor read as zero
+// (out-of-range buffer offsets).
+// ---------------------------------------------------------------------------
+namespace sk {
+constexpr int DT = 128;   // down: tokens per workgroup (32 per wave)
+constexpr int DK = 64;    // down: k per stage
+constexpr int TJ = 128;   // token: columns per workgroup (32 per wave)
+constexpr int TS = 64;    // token: tokens per stage
+}  // namespace sk
+
+// s_waitcnt vmcnt(N) with the other counters unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// One direct-to-LDS load of 16 bytes per lane: lane l writes bytes
+// 16 l .. 16 l + 15 of the 1 KB block at `blk`.
+__device__ __forceinline__ void dma16(brsrc_t r, uint8_t* blk, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)blk, 16, voff, 0, 0, 0);
+}
+
+// 16-byte chunk c (0..7) of row `row` in a tile of 128-byte rows sits at
+// slot c ^ (row % 8): 16x16x32 fragment reads and 1 KB block writes are free
+// of bank conflicts.
+__device__ __forceinline__ uint32_t sw128(int row, int c) { return (uint32_t)(row * 128 + ((c ^ (row & 7)) << 4)); }
+
+// Workgroup barrier without __syncthreads' memory fence, which the compiler
+// lowers to a wait for every load in flight (the whole ring).  The ring's
+// own vmcnt wait makes this wave's loads of the stage complete, the barrier
+// makes every wave's, and LDS needs no cache maintenance; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The ring: stage s lives in buffer s % NS; step s waits for stage s, issues
+// stage s + NS - 1 into the buffer of stage s - 1 (free after the barrier)
+// and computes stage s.  Loads are issued unconditionally: stages past the
+// end read only out-of-range offsets (zeros, no memory traffic) into buffers
+// nobody reads again.  So before the wait of step s exactly the stages
+// s .. s + NS - 2 are in flight, and since loads retire in order, allowing
+// the later stages' loads to stay outstanding leaves stage s complete (LMIN:
+// the loads every wave issues per stage; waves that issue more only wait
+// longer).  A conditional issue would make the compiler wait for every load
+// in flight where the paths meet, so the steady-state loop runs whole rings
+// and the remaining steps follow it.  The final wait keeps late loads from
+// writing LDS after the workgroup has ended.
+template <int NS, int LMIN, typename Issue, typename Compute>
+__device__ __forceinline__ void ring_run(int nst, uint8_t* const (&buf)[NS], Issue issue, Compute compute) {
+  static_assert(NS >= 3 && NS <= 4, "ring depth");
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u) issue(u, buf[u]);
+  auto step = [&](int s, int u) {
+    wait_vmcnt<LMIN * (NS - 2)>();
+    ring_barrier();
+    issue(s + NS - 1, buf[(u + NS - 1) % NS]);
+    compute(buf[u]);
+  };
+  const int full = nst - nst % NS;
+  for (int s0 = 0; s0 < full; s0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(s0 + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (full + u < nst) step(full + u, u);
+  wait_vmcnt<0>();
+}
+
+template <int RB, int NS>
+__global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                          const uint16_t* __restrict__ Y, int R,
+                                                          float* __restrict__ part, int64_t kc) {
+  // Rank rows come in 1 KB blocks of 8, YPW per wave: 16 RB rows, or 32 for
+  // RB = 1 (every wave issues the same loads; rows past R read zeros).
+  constexpr int YPW = RB >= 2 ? RB / 2 : 1;
+  constexpr int XB = sk::DT * 128;     // 128 token rows x 64 k
+  constexpr int YB = 4 * YPW * 1024;   // 32 YPW rank rows x 64 k
+  constexpr int STAGE = XB + YB;
+  __shared__ __align__(16) uint8_t s0[STAGE];
+  __shared__ __align__(16) uint8_t s1[STAGE];
+  __shared__ __align__(16) uint8_t s2[NS > 2 ? STAGE : 16];
+  __shared__ __align__(16) uint8_t s3[NS > 3 ? STAGE : 16];
+  uint8_t* const buf4[4] = {s0, s1, s2, s3};
+  uint8_t* buf[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) buf[i] = buf4[i];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * sk::DT;
+  const int split = blockIdx.y;
+  const int64_t kbeg = (int64_t)split * kc;
+  const int64_t kend = (kbeg + kc < K) ? kbeg + kc : K;
+  const int nst = (int)cdiv(kend - kbeg, sk::DK);
+  const uint32_t xbytes = (uint32_t)(M * K * 2);
+  const uint32_t ybytes = (uint32_t)((int64_t)R * K * 2);
+  const brsrc_t rx = make_rsrc(X, xbytes);
+  const brsrc_t ry = make_rsrc(Y, ybytes);
+  // A 1 KB load block is 8 rows of 128 B: lane l lands in row l / 8, slot
+  // l % 8, which holds chunk (l % 8) ^ (l / 8) of its row (sw128).
+  const int drow = lane >> 3;
+  const int64_t kl = kbeg + 8 * ((lane & 7) ^ drow);
+  constexpr int LMIN = 4 + YPW;
+  auto issue = [&](int s, uint8_t* stg) {
+    const int64_t k = kl + (int64_t)s * sk::DK;
+    const bool kok = k < kend;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // this wave's token rows 32 w .. 32 w + 31
+      const int64_t t = t0 + 32 * wave + 8 * b + drow;
+      dma16(rx, stg + (32 * wave + 8 * b) * 128, (kok && t < M) ? (uint32_t)((t * K + k) * 2) : xbytes);
+    }
+#pragma unroll
+    for (int j = 0; j < YPW; ++j) {
+      const int blk = wave + 4 * j;
+      const int q = 8 * blk + drow;
+      dma16(ry, stg + XB + blk * 1024, (kok && q < R) ? (uint32_t)(((int64_t)q * K + k) * 2) : ybytes);
+    }
+  };
+  f32x4 acc[2][RB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < RB; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* stg) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 bq[RB];
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb)
+        bq[cb] = *reinterpret_cast<const u32x4*>(stg + XB + sw128(16 * cb + lr, 4 * kk + lq));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(stg + sw128(32 * wave + 16 * i + lr, 4 * kk + lq));
+#pragma unroll
+        for (int cb = 0; cb < RB; ++cb) acc[i][cb] = mfma16x16x32(a, bq[cb], acc[i][cb]);
+      }
+    }
+  };
+  ring_run<NS, LMIN>(nst, buf, issue, compute);
+
+  // lane holds tokens 32 w + 16 i + 4 lq + e, rank 16 cb + lr
+  float* dst = part + (int64_t)split * M * R;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int cb = 0; cb < RB; ++cb) {
+      const int q = 16 * cb + lr;
+      if (q >= R) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = t0 + 32 * wave + 16 * i + 4 * lq + e;
+        if (t < M) dst[t * R + q] = acc[i][cb][e];
+      }
+    }
+}
+
+template <int RB, int NS>
+__global__ __launch_bounds__(256) void skinny_token_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t J,
+                                                           const uint16_t* __restrict__ P, int64_t Mp, int R,
+                                                           float* __restrict__ part, int64_t tc) {
+  constexpr int XB = sk::TS * 256;     // 64 token rows x 128 columns
+  constexpr int PB = RB * 16 * 128;    // one plane: 16 RB rank rows x 64 tokens
+  constexpr int STAGE = XB + 2 * PB;
+  __shared__ __align__(16) uint8_t s0[STAGE];
+  __shared__ __align__(16) uint8_t s1[STAGE];
+  __shared__ __align__(16) uint8_t s2[NS > 2 ? STAGE : 16];
+  __shared__ __align__(16) uint8_t s3[NS > 3 ? STAGE : 16];
+  uint8_t* const buf4[4] = {s0, s1, s2, s3};
+  uint8_t* buf[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) buf[i] = buf4[i];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int64_t j0 = (int64_t)blockIdx.x * sk::TJ;
+  const int split = blockIdx.y;
+  const int64_t tbeg = (int64_t)split * tc;
+  const int64_t tend = (tbeg + tc < M) ? tbeg + tc : M;
+  const int nst = (int)cdiv(tend - tbeg, sk::TS);
+  const uint32_t xbytes = (uint32_t)(M * J * 2);
+  const uint32_t pbytes = (uint32_t)(2 * (int64_t)R * Mp * 2);
+  const brsrc_t rx = make_rsrc(X, xbytes);
+  const brsrc_t rp = make_rsrc(P, pbytes);
+  // X: a 1 KB load block is 4 token rows of 256 B; lane l lands in row l / 16
+  // at 16-byte slot l % 16, which holds piece c of the row with
+  // (c / 2) ^ f(row) == slot / 2 and c % 2 == slot % 2 (swtg).
+  const int xrow = lane >> 4;
+  const int slot = lane & 15;
+  // Planes: a 1 KB block is 8 rank rows of 128 B; lane l lands in row l / 8,
+  // slot l % 8, which holds chunk (l % 8) ^ ((q / 2) % 8) (swy).
+  const int prow = lane >> 3;
+  constexpr int LMIN = 4 + RB;
+  auto issue = [&](int s, uint8_t* stg) {
+    const int64_t tb = tbeg + (int64_t)s * sk::TS;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // rows 16 w .. 16 w + 15 of the stage
+      const int blk = 4 * wave + b;
+      const int row = 4 * blk + xrow;
+      const int f = (row & 3) | (((row >> 3) & 1) << 2);
+      const int c = ((((slot >> 1) ^ f)) << 1) | (slot & 1);
+      const int64_t t = tb + row;
+      const int64_t j = j0 + 8 * c;
+      dma16(rx, stg + blk * 1024, (t < tend && j < J) ? (uint32_t)((t * J + j) * 2) : xbytes);
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {  // blocks 4 b + w of the two planes (2 RB blocks each)
+      const int id = 4 * b + wave;
+      const int pl = id / (2 * RB);
+      const int q = 8 * (id % (2 * RB)) + prow;
+      const int c = (lane & 7) ^ ((q >> 1) & 7);
+      dma16(rp, stg + XB + pl * PB + (id % (2 * RB)) * 1024,
+            (q < R && tb < tend) ? (uint32_t)((((int64_t)pl * R + q) * Mp + tb + 8 * c) * 2) : pbytes);
+    }
+  };
+  f32x4 acc[2][RB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < RB; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tr_row = lr >> 2;
+  const int tr_c = lr & 3;
+  auto compute = [&](const uint8_t* stg) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 a[2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        // lanes 4 r + c of each 16-lane group address token row r, columns 4 c .. 4 c + 3
+        const int t = 32 * kk + 8 * lq + tr_row;
+        const int c = 2 * (2 * wave + ib) + (tr_c >> 1);
+        const uint8_t* p0 = stg + swtg(t, c) + (tr_c & 1) * 8;
+        const uint8_t* p1 = stg + swtg(t + 4, c) + (tr_c & 1) * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        a[ib] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+      }
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) {
+        const uint32_t off = swy(16 * cb + lr, 4 * kk + lq);
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(stg + XB + off);
+        const u32x4 bl = *reinterpret_cast<const u32x4*>(stg + XB + PB + off);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          acc[ib][cb] = mfma16x16x32(a[ib], bh, acc[ib][cb]);
+          acc[ib][cb] = mfma16x16x32(a[ib], bl, acc[ib][cb]);
+        }
+      }
+    }
+  };
+  ring_run<NS, LMIN>(nst, buf, issue, compute);
+
+  // lane holds columns j = 32 w + 16 ib + 4 lq + e, rank q = 16 cb + lr
+  float* dst = part + (int64_t)split * J * R;
+#pragma unroll
+  for (int cb = 0; cb < RB; ++cb) {
+    const int q = 16 * cb + lr;
+    if (q >= R) continue;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = j0 + 32 * wave + 16 * ib + 4 * lq + e;
+        if (j < J) dst[j * R + q] = acc[ib][cb][e];
+      }
+  }
+}
+
+// P[0][q][t] = bf16(Y[t][q]), P[1][q][t] = bf16(Y[t][q] - P[0][q][t]) (the
+// fp32 factor as bf16 hi + lo, transposed), zero for M <= t < Mp.  A
+// workgroup takes 64 tokens: their rows of Y are staged in LDS, then every
+// thread writes 8 consecutive tokens of one plane row.
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ Y, int64_t M, int R,
+                                                           int64_t Mp, uint16_t* __restrict__ P) {
+  __shared__ float sy[64][kMaxRank + 1];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * R; i += 256) {
+    const int t = i / R, q = i % R;
+    sy[t][q] = t0 + t < M ? Y[(t0 + t) * R + q] : 0.0f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * R * 8; i += 256) {
+    const int c = i & 7;
+    const int q = (i >> 3) % R;
+    const int pl = (i >> 3) / R;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float h0, l0, h1, l1;
+      split_bf16(sy[8 * c + 2 * e][q], h0, l0);
+      split_bf16(sy[8 * c + 2 * e + 1][q], h1, l1);
+      w[e] = pl ? pack_bf16x2(l0, l1) : pack_bf16x2(h0, h1);
+    }
+    *reinterpret_cast<u32x4*>(P + ((int64_t)pl * R + q) * Mp + t0 + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launch helpers
 // ---------------------------------------------------------------------------
 static inline int rank_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8; }
-// Workgroups wanted per launch: enough to cover every CU a few times over
-// (fewer for the large-rank variants, which hold one workgroup per CU).
-static inline int64_t target_wgs(int R) { return rank_blocks(R) <= 2 ? 512 : 256; }
+// LDS ring depth of the streaming token kernel: three stages while two
+// workgroups fit a CU, four when the hi / lo planes make a stage 32 KB.
+static inline int token_stages(int R) { return rank_blocks(R) == 4 ? 4 : 3; }
+// Workgroups that fit one CU (160 KB of LDS) for the streaming kernels.
+static inline int down_wgs_per_cu(int R) { return rank_blocks(R) <= 4 ? 2 : 1; }
+static inline int token_wgs_per_cu(int R) { return rank_blocks(R) <= 2 ? 2 : 1; }
 
+// K splits of a down product: enough 128-token tiles x splits to fill every
+// CU with its resident workgroups, at most 64 splits, each at least 512 k
+// long and a multiple of 128 (the masked kernel takes 128-k stages).
 int down_proj_splits(int64_t M, int64_t K, int R) {
-  const int64_t tiles = cdiv(M, dp::TT);
-  const int64_t stages = cdiv(K, dp::KCH);
-  int64_t want = cdiv(target_wgs(R), tiles);
-  if (want < 1) want = 1;
-  if (want > stages) want = stages;
+  const int64_t tiles = cdiv(M, sk::DT);
+  int64_t want = cdiv((int64_t)down_wgs_per_cu(R) * device_cus(), tiles);
+  const int64_t most = cdiv(K, 512);
+  if (want > most) want = most;
   if (want > 64) want = 64;
+  if (want < 1) want = 1;
   return (int)cdiv(K, cdiv(cdiv(K, want), dp::KCH) * dp::KCH);
 }
 
 // drop: dropout on X (the adapter input), or null; the result is scaled by
-// `scale` (1 / (1 - p) with dropout) after the fixed-order sum
+// `scale` (1 / (1 - p) with dropout) after the fixed-order sum.  Unmasked
+// products stream through skinny_down_kernel; masked ones take
+// down_proj_kernel, which applies the mask between its loads and LDS stores.
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
                       float* out, hipStream_t stream, const DropoutDev* drop, float scale) {
   const int64_t kc = cdiv(cdiv(K, splits), dp::KCH) * dp::KCH;
-  const dim3 grid((unsigned)cdiv(M, dp::TT), (unsigned)splits);
-  const DropoutDev d = drop ? *drop : DropoutDev{0u, 0u, 0u, 0ull, 0};
-  switch (rank_blocks(R)) {
-    case 1: hipLaunchKernelGGL(down_proj_kernel<1>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
-    case 2: hipLaunchKernelGGL(down_proj_kernel<2>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
-    case 4: hipLaunchKernelGGL(down_proj_kernel<4>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
-    default: hipLaunchKernelGGL(down_proj_kernel<8>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+  if (drop && drop->on) {
+    const dim3 grid((unsigned)cdiv(M, dp::TT), (unsigned)splits);
+    const DropoutDev d = *drop;
+    switch (rank_blocks(R)) {
+      case 1: hipLaunchKernelGGL(down_proj_kernel<1>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+      case 2: hipLaunchKernelGGL(down_proj_kernel<2>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+      case 4: hipLaunchKernelGGL(down_proj_kernel<4>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+      default: hipLaunchKernelGGL(down_proj_kernel<8>, grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, d); break;
+    }
+  } else {
+    const dim3 grid((unsigned)cdiv(M, sk::DT), (unsigned)splits);
+    switch (rank_blocks(R)) {
+      case 1: hipLaunchKernelGGL((skinny_down_kernel<1, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 2: hipLaunchKernelGGL((skinny_down_kernel<2, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 4: hipLaunchKernelGGL((skinny_down_kernel<4, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      default: hipLaunchKernelGGL((skinny_down_kernel<8, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+    }
   }
   const int64_t count = M * R;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
                      count, scale, out);
 }
 
+// Token splits of a reduction over tokens: enough 128-column tiles x splits
+// to fill every CU, at most 64 splits of at least 512 tokens (multiples of 64).
 int token_grad_splits(int64_t M, int64_t J, int R) {
   const int64_t tiles = cdiv(J, tg::JT);
-  const int64_t stages = cdiv(M, tg::TT);
-  int64_t want = cdiv(target_wgs(R), tiles);
-  if (want < 1) want = 1;
-  if (want > stages) want = stages;
+  int64_t want = cdiv((int64_t)token_wgs_per_cu(R) * device_cus(), tiles);
+  const int64_t most = cdiv(M, 512);
+  if (want > most) want = most;
   if (want > 64) want = 64;
+  if (want < 1) want = 1;
   return (int)cdiv(M, cdiv(cdiv(M, want), tg::TT) * tg::TT);
 }
 
+// Bytes of the bf16 hi / lo planes of an M x R factor (token pitch M rounded
+// up to 64).
+size_t token_planes_bytes(int64_t M, int R) { return (size_t)2 * R * (size_t)(cdiv(M, 64) * 64) * 2; }
+
+// out = bf16(s sum_t X[t][j] Y[t][q]) over the first Jout columns.  Unmasked
+// reductions split Y into bf16 hi / lo planes (`planes`, token_planes_bytes)
+// and stream through skinny_token_kernel; masked ones (drop on) take
+// token_grad_kernel.
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
                        int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop) {
+                       const DropoutDev* drop, uint16_t* planes) {
   const int64_t tc = cdiv(cdiv(M, splits), tg::TT) * tg::TT;
   const dim3 grid((unsigned)cdiv(J, tg::JT), (unsigned)splits);
-  const DropoutDev d = drop ? *drop : DropoutDev{0u, 0u, 0u, 0ull, 0};
-  switch (rank_blocks(R)) {
-    case 1: hipLaunchKernelGGL(token_grad_kernel<1>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
-    case 2: hipLaunchKernelGGL(token_grad_kernel<2>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
-    case 4: hipLaunchKernelGGL(token_grad_kernel<4>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
-    default: hipLaunchKernelGGL(token_grad_kernel<8>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+  if (drop && drop->on) {
+    const DropoutDev d = *drop;
+    switch (rank_blocks(R)) {
+      case 1: hipLaunchKernelGGL(token_grad_kernel<1>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+      case 2: hipLaunchKernelGGL(token_grad_kernel<2>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+      case 4: hipLaunchKernelGGL(token_grad_kernel<4>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+      default: hipLaunchKernelGGL(token_grad_kernel<8>, grid, dim3(256), 0, stream, X, M, J, Y, R, part, tc, d); break;
+    }
+  } else {
+    const int64_t Mp = cdiv(M, 64) * 64;
+    hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)(Mp / 64)), dim3(256), 0, stream, Y, M, R, Mp, planes);
+    switch (rank_blocks(R)) {
+      case 1: hipLaunchKernelGGL((skinny_token_kernel<1, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
+      case 2: hipLaunchKernelGGL((skinny_token_kernel<2, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
+      case 4: hipLaunchKernelGGL((skinny_token_kernel<4, 4>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
+      default: hipLaunchKernelGGL((skinny_token_kernel<8, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
+    }
   }
   const int64_t count = Jout * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,

@@ -23,6 +23,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Host: compute units of the current device (cached per device).
+int device_cus();
+
 constexpr int kBlock = 64;        // weights per absmax block
 constexpr int kGroupBlocks = 256; // blocks per double-quant group
 constexpr int kMaxRank = 128;
