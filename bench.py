@@ -483,6 +483,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the measurements outside the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--small-only", action="store_true",
+                    help="only run the small-token section (for profiling it alone)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -506,6 +508,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+
+    if args.small_only:
+        print(json.dumps({"small_tokens": small_token_block(Q, dev, max(args.steps, 3))}), flush=True)
         return
 
     cfg = 5

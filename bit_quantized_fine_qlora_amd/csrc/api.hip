@@ -53,8 +53,10 @@ void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y
 int token_grad_splits(int64_t M, int64_t J, int R);
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
                        int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop, uint16_t* planes);
+                       const DropoutDev* drop, uint16_t* planes, bool planes_ready);
 size_t token_planes_bytes(int64_t M, int R);
+void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t* P, float* Yout, const float* Y2,
+                          uint16_t* P2, hipStream_t stream);
 void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
                               const DropoutDev& drop, float* out, hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
@@ -261,7 +263,7 @@ FwdWs fwd_ws(int64_t M, int64_t n, int64_t m, int32_t r) {
 }
 
 struct BwdWs {
-  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, planes, ksplit, total;
+  size_t Bt, part_uv, u, v, gA, gB, gpad, vpart, gbpart, dterm, planes, uplanes, ksplit, total;
   int su, sv, sa, sb;
   bool gpass;     // v and grad_B from one read of g
   bool has_ksplit;
@@ -292,8 +294,9 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
   // dropout: the masked adapter part of grad_x in fp32
   w.dterm = dropout ? L.take((size_t)M * n * sizeof(float)) : 0;
-  // bf16 hi / lo planes of u (grad_B) and then of v (grad_A)
+  // bf16 hi / lo planes of v (grad_A) and, without the g pass, of u (grad_B)
   w.planes = L.take(token_planes_bytes(M, r));
+  w.uplanes = w.gpass ? 0 : L.take(token_planes_bytes(M, r));
   // grad_x GEMM tiles split in K (few tiles, or a short last round)
   const size_t kb = gemm_split_ws_bytes(M, n, w.m_pad);
   w.ksplit = kb ? L.take(kb) : 0;
@@ -698,32 +701,39 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     uu = at<float>(workspace, w.u);
   }
   float* v = at<float>(workspace, w.v);
+  uint16_t* vplanes = at<uint16_t>(workspace, w.planes);
   if (w.gpass) {
-    // v = g B and grad_B = s g^T u from one read of g
+    // v = g B and grad_B = s g^T u from one read of g; then v (the sum of
+    // its partials) with its bf16 planes for grad_A in one launch
     Timed tm("gpass", hs);
-    launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), v,
+    launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), nullptr,
                  grad_B, hs);
+    launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(mk, r), M, r, vplanes, v, nullptr, nullptr,
+                         hs);
   } else {
     uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
+    uint16_t* uplanes = at<uint16_t>(workspace, w.uplanes);
     {
       Timed tm("transpose", hs);
       launch_transpose_bf16(B, m, r, mk, Bt, hs);
     }
     {
+      // v partials; then v, its planes and u's planes in one launch
       Timed tm("down_proj", hs);
-      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, v, hs, nullptr, 1.0f);
+      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, nullptr, hs, nullptr, 1.0f);
+      launch_factor_planes(part, w.sv, M, r, vplanes, v, uu, uplanes, hs);
     }
     {
       Timed tm("token_grad", hs);
-      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr,
-                        at<uint16_t>(workspace, w.planes));
+      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr, uplanes,
+                        true);
     }
   }
   {
     Timed tm("token_grad", hs);
     // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p)
-    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd,
-                      at<uint16_t>(workspace, w.planes));
+    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd, vplanes,
+                      true);
   }
   if (grad_x) {
     if (drop) {

@@ -623,7 +623,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 // (no registers in between, no LDS store instructions), the small operand
 // rides along the same way in bf16: A or B^T for the down products; for the
 // token products the fp32 factor (u or v) as bf16 hi and lo planes [q][t],
-// written once per call by split_planes_kernel.  Each stage is a separate
+// written once per call by factor_planes_kernel.  Each stage is a separate
 // LDS array and every loop over the ring is unrolled by NS, so the compiler
 // sees which stage each fragment read touches and does not make it wait for
 // the loads in flight into the other stages.  A wave waits only for its own
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 namespace sk {
 constexpr int DT = 128;   // down: tokens per workgroup (32 per wave)
-constexpr int DK = 64;    // down: k per stage
+constexpr int DCH = 8;    // down: 16-byte chunks per token row and stage (8 CH k)
 constexpr int TJ = 128;   // token: columns per workgroup (32 per wave)
 constexpr int TS = 64;    // token: tokens per stage
 }  // namespace sk
@@ -702,15 +702,28 @@ __device__ __forceinline__ void ring_run(int nst, uint8_t* const (&buf)[NS], Iss
   wait_vmcnt<0>();
 }
 
-template <int RB, int NS>
+// CH 16-byte chunks (8 CH k) per token row and stage: chunk c of row r
+// sits at slot c ^ (r % CH), so 16x16x32 fragment reads are conflict-free.
+template <int CH>
+__device__ __forceinline__ uint32_t swch(int row, int c) {
+  return (uint32_t)(row * (16 * CH) + ((c ^ (row & (CH - 1))) << 4));
+}
+
+template <int RB, int NS, int CH>
 __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                           const uint16_t* __restrict__ Y, int R,
                                                           float* __restrict__ part, int64_t kc) {
-  // Rank rows come in 1 KB blocks of 8, YPW per wave: 16 RB rows, or 32 for
-  // RB = 1 (every wave issues the same loads; rows past R read zeros).
-  constexpr int YPW = RB >= 2 ? RB / 2 : 1;
-  constexpr int XB = sk::DT * 128;     // 128 token rows x 64 k
-  constexpr int YB = 4 * YPW * 1024;   // 32 YPW rank rows x 64 k
+  static_assert(CH == 8 || CH == 16, "row chunks per stage");
+  constexpr int KS = 8 * CH;               // k per stage
+  constexpr int RPB = 64 / CH;             // rows per 1 KB load block
+  constexpr int XPW = 32 / RPB;            // X blocks per wave (its 32 token rows)
+  // Rank rows: 16 RB rows of CH chunks, in 1 KB blocks, YPW per wave (every
+  // wave issues the same number of loads; blocks past the rank rows read
+  // zeros into the padding)
+  constexpr int YBLK = (16 * RB) / RPB;
+  constexpr int YPW = YBLK >= 4 ? YBLK / 4 : 1;
+  constexpr int XB = sk::DT * 16 * CH;     // 128 token rows x KS k
+  constexpr int YB = 4 * YPW * 1024;
   constexpr int STAGE = XB + YB;
   __shared__ __align__(16) uint8_t s0[STAGE];
   __shared__ __align__(16) uint8_t s1[STAGE];
@@ -729,29 +742,31 @@ __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __rest
   const int split = blockIdx.y;
   const int64_t kbeg = (int64_t)split * kc;
   const int64_t kend = (kbeg + kc < K) ? kbeg + kc : K;
-  const int nst = (int)cdiv(kend - kbeg, sk::DK);
+  const int nst = (int)cdiv(kend - kbeg, KS);
   const uint32_t xbytes = (uint32_t)(M * K * 2);
   const uint32_t ybytes = (uint32_t)((int64_t)R * K * 2);
   const brsrc_t rx = make_rsrc(X, xbytes);
   const brsrc_t ry = make_rsrc(Y, ybytes);
-  // A 1 KB load block is 8 rows of 128 B: lane l lands in row l / 8, slot
-  // l % 8, which holds chunk (l % 8) ^ (l / 8) of its row (sw128).
-  const int drow = lane >> 3;
-  const int64_t kl = kbeg + 8 * ((lane & 7) ^ drow);
-  constexpr int LMIN = 4 + YPW;
+  // A 1 KB load block holds RPB rows: lane l lands in row l / CH of the
+  // block at slot l % CH, which holds chunk (l % CH) ^ (row % CH) (swch).
+  const int drow = lane / CH;
+  const int dslot = lane % CH;
+  constexpr int LMIN = XPW + YPW;
   auto issue = [&](int s, uint8_t* stg) {
-    const int64_t k = kl + (int64_t)s * sk::DK;
-    const bool kok = k < kend;
+    const int64_t kb = kbeg + (int64_t)s * KS;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {  // this wave's token rows 32 w .. 32 w + 31
-      const int64_t t = t0 + 32 * wave + 8 * b + drow;
-      dma16(rx, stg + (32 * wave + 8 * b) * 128, (kok && t < M) ? (uint32_t)((t * K + k) * 2) : xbytes);
+    for (int b = 0; b < XPW; ++b) {  // this wave's token rows 32 w .. 32 w + 31
+      const int row = 32 * wave + RPB * b + drow;
+      const int64_t k = kb + 8 * (dslot ^ (row & (CH - 1)));
+      const int64_t t = t0 + row;
+      dma16(rx, stg + (32 * wave + RPB * b) * (16 * CH), (k < kend && t < M) ? (uint32_t)((t * K + k) * 2) : xbytes);
     }
 #pragma unroll
     for (int j = 0; j < YPW; ++j) {
       const int blk = wave + 4 * j;
-      const int q = 8 * blk + drow;
-      dma16(ry, stg + XB + blk * 1024, (kok && q < R) ? (uint32_t)(((int64_t)q * K + k) * 2) : ybytes);
+      const int q = RPB * blk + drow;
+      const int64_t k = kb + 8 * (dslot ^ (q & (CH - 1)));
+      dma16(ry, stg + XB + blk * 1024, (k < kend && q < R) ? (uint32_t)(((int64_t)q * K + k) * 2) : ybytes);
     }
   };
   f32x4 acc[2][RB];
@@ -761,14 +776,14 @@ __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __rest
     for (int c = 0; c < RB; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const uint8_t* stg) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < CH / 4; ++kk) {
       u32x4 bq[RB];
 #pragma unroll
       for (int cb = 0; cb < RB; ++cb)
-        bq[cb] = *reinterpret_cast<const u32x4*>(stg + XB + sw128(16 * cb + lr, 4 * kk + lq));
+        bq[cb] = *reinterpret_cast<const u32x4*>(stg + XB + swch<CH>(16 * cb + lr, 4 * kk + lq));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(stg + sw128(32 * wave + 16 * i + lr, 4 * kk + lq));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(stg + swch<CH>(32 * wave + 16 * i + lr, 4 * kk + lq));
 #pragma unroll
         for (int cb = 0; cb < RB; ++cb) acc[i][cb] = mfma16x16x32(a, bq[cb], acc[i][cb]);
       }
@@ -907,17 +922,33 @@ __global__ __launch_bounds__(256) void skinny_token_kernel(const uint16_t* __res
   }
 }
 
-// P[0][q][t] = bf16(Y[t][q]), P[1][q][t] = bf16(Y[t][q] - P[0][q][t]) (the
-// fp32 factor as bf16 hi + lo, transposed), zero for M <= t < Mp.  A
-// workgroup takes 64 tokens: their rows of Y are staged in LDS, then every
-// thread writes 8 consecutive tokens of one plane row.
-__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ Y, int64_t M, int R,
-                                                           int64_t Mp, uint16_t* __restrict__ P) {
+// bf16 hi / lo planes of an fp32 M x R factor, transposed:
+//   P[0][q][t] = bf16(Y[t][q]),  P[1][q][t] = bf16(Y[t][q] - P[0][q][t]),
+// zero for M <= t < Mp.  Grid y = 0 makes the planes of Y = sum of `nsplit`
+// fp32 partials (stride M R, added in split order from 0, as
+// reduce_splits_kernel adds them) and, if Yout is given, also writes that
+// sum; grid y = 1 makes the planes P2 of a second factor Y2 (one part).  A
+// workgroup takes 64 tokens: their rows are staged in LDS, then every thread
+// writes 8 consecutive tokens of one plane row.
+__global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restrict__ Y, int nsplit, int64_t M, int R,
+                                                            int64_t Mp, uint16_t* __restrict__ P,
+                                                            float* __restrict__ Yout, const float* __restrict__ Y2,
+                                                            uint16_t* __restrict__ P2) {
   __shared__ float sy[64][kMaxRank + 1];
   const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const bool second = blockIdx.y == 1;
+  const float* src = second ? Y2 : Y;
+  const int ns = second ? 1 : nsplit;
+  uint16_t* dstp = second ? P2 : P;
   for (int i = threadIdx.x; i < 64 * R; i += 256) {
     const int t = i / R, q = i % R;
-    sy[t][q] = t0 + t < M ? Y[(t0 + t) * R + q] : 0.0f;
+    float acc = 0.0f;
+    if (t0 + t < M) {
+      const int64_t idx = (t0 + t) * R + q;
+      acc = sum_splits(src, ns, M * R, idx);
+      if (!second && Yout) Yout[idx] = acc;
+    }
+    sy[t][q] = acc;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 2 * R * 8; i += 256) {
@@ -932,7 +963,7 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restri
       split_bf16(sy[8 * c + 2 * e + 1][q], h1, l1);
       w[e] = pl ? pack_bf16x2(l0, l1) : pack_bf16x2(h0, h1);
     }
-    *reinterpret_cast<u32x4*>(P + ((int64_t)pl * R + q) * Mp + t0 + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dstp + ((int64_t)pl * R + q) * Mp + t0 + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -961,7 +992,8 @@ int down_proj_splits(int64_t M, int64_t K, int R) {
 }
 
 // drop: dropout on X (the adapter input), or null; the result is scaled by
-// `scale` (1 / (1 - p) with dropout) after the fixed-order sum.  Unmasked
+// `scale` (1 / (1 - p) with dropout) after the fixed-order sum; with out
+// null only the split partials are written.  Unmasked
 // products stream through skinny_down_kernel; masked ones take
 // down_proj_kernel, which applies the mask between its loads and LDS stores.
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
@@ -978,13 +1010,15 @@ void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y
     }
   } else {
     const dim3 grid((unsigned)cdiv(M, sk::DT), (unsigned)splits);
+    constexpr int CH = sk::DCH;
     switch (rank_blocks(R)) {
-      case 1: hipLaunchKernelGGL((skinny_down_kernel<1, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      case 2: hipLaunchKernelGGL((skinny_down_kernel<2, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      case 4: hipLaunchKernelGGL((skinny_down_kernel<4, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      default: hipLaunchKernelGGL((skinny_down_kernel<8, 3>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 1: hipLaunchKernelGGL((skinny_down_kernel<1, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 2: hipLaunchKernelGGL((skinny_down_kernel<2, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 4: hipLaunchKernelGGL((skinny_down_kernel<4, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      default: hipLaunchKernelGGL((skinny_down_kernel<8, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
     }
   }
+  if (!out) return;  // the caller sums the partials (factor_planes_kernel)
   const int64_t count = M * R;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
                      count, scale, out);
@@ -1006,13 +1040,22 @@ int token_grad_splits(int64_t M, int64_t J, int R) {
 // up to 64).
 size_t token_planes_bytes(int64_t M, int R) { return (size_t)2 * R * (size_t)(cdiv(M, 64) * 64) * 2; }
 
+// Planes of Y = sum of nsplit partials (written to Yout when given) and, if
+// Y2 is given, of Y2; token_planes_bytes each.
+void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t* P, float* Yout, const float* Y2,
+                          uint16_t* P2, hipStream_t stream) {
+  const int64_t Mp = cdiv(M, 64) * 64;
+  hipLaunchKernelGGL(factor_planes_kernel, dim3((unsigned)(Mp / 64), Y2 ? 2u : 1u), dim3(256), 0, stream, Y, nsplit,
+                     M, R, Mp, P, Yout, Y2, P2);
+}
+
 // out = bf16(s sum_t X[t][j] Y[t][q]) over the first Jout columns.  Unmasked
-// reductions split Y into bf16 hi / lo planes (`planes`, token_planes_bytes)
-// and stream through skinny_token_kernel; masked ones (drop on) take
-// token_grad_kernel.
+// reductions stream through skinny_token_kernel from Y's bf16 hi / lo planes
+// (`planes`, token_planes_bytes), made here unless planes_ready; masked ones
+// (drop on) take token_grad_kernel, which reads Y itself.
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
                        int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop, uint16_t* planes) {
+                       const DropoutDev* drop, uint16_t* planes, bool planes_ready) {
   const int64_t tc = cdiv(cdiv(M, splits), tg::TT) * tg::TT;
   const dim3 grid((unsigned)cdiv(J, tg::JT), (unsigned)splits);
   if (drop && drop->on) {
@@ -1025,7 +1068,7 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
     }
   } else {
     const int64_t Mp = cdiv(M, 64) * 64;
-    hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)(Mp / 64)), dim3(256), 0, stream, Y, M, R, Mp, planes);
+    if (!planes_ready) launch_factor_planes(Y, 1, M, R, planes, nullptr, nullptr, nullptr, stream);
     switch (rank_blocks(R)) {
       case 1: hipLaunchKernelGGL((skinny_token_kernel<1, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
       case 2: hipLaunchKernelGGL((skinny_token_kernel<2, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
@@ -1125,9 +1168,11 @@ void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, in
     hipLaunchKernelGGL((gpass_kernel<1, 4>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
   else
     hipLaunchKernelGGL((gpass_kernel<2, 2>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
-  const int64_t count = M * R;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
-                     1.0f, v);
+  if (v) {  // else the caller sums the v partials (factor_planes_kernel)
+    const int64_t count = M * R;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
+                       1.0f, v);
+  }
   const int64_t gcount = m * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(gcount, 256)), dim3(256), 0, stream, gbpart, st, J, m,
                      R, s, 0, grad_B);

@@ -159,6 +159,7 @@ def test_linear_check_without_hand_off(lib):
     # nothing read back (no GPU is touched); bad arguments are rejected first
     f = lib.qlora_linear_check
     assert f(0, 16, 4096, 1024, 16, None, None) == 0       # weight-streaming forward
+    assert f(1, 16, 4096, 1024, 16, None, None) == 0       # 16 grad_x tiles: K pieces, no wait
     assert f(0, 4096, 4096, 4096, 16, None, None) == 0     # 256 tiles: one full round
     assert f(1, 256, 4096, 14336, 16, None, None) == 0     # few tiles: K pieces, no wait
     assert f(3, 4096, 4096, 4096, 16, None, None) == -7    # unknown op
