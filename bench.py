@@ -63,9 +63,27 @@ BF16_PEAK_TFLOPS = 2500.0
 # 2.0, WRITE_SIZE x 1.0; see profiles/).  Keyed by "layer/kernel" of the
 # 70B-block step.  Valid only for the GEMM sources they were taken on (the
 # kernel and the header it includes): reported as null once either changes.
+# The counters count the L2's requests to the memory fabric, so bytes served
+# by the last-level cache (MALL) are included: an upper bound on HBM bytes.
+# The k and v forwards are few-tile launches whose writes are the fp32 K
+# pieces, not h.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": None,
+    "src_sha1": "177549dbae367d2ff665f06957fc786270183bcf",
+    "q/fwd_gemm": {"fetch": 1297420843, "write": 134250837},
+    "k/fwd_gemm": {"fetch": 550731136, "write": 67108864},
+    "v/fwd_gemm": {"fetch": 550768597, "write": 67108864},
+    "o/fwd_gemm": {"fetch": 1296333525, "write": 134255531},
+    "gate/fwd_gemm": {"fetch": 4817727701, "write": 469857195},
+    "up/fwd_gemm": {"fetch": 4826893227, "write": 469820544},
+    "down/fwd_gemm": {"fetch": 4459527339, "write": 134222635},
+    "down/dgrad_gemm": {"fetch": 4604059349, "write": 469778347},
+    "up/dgrad_gemm": {"fetch": 4383778987, "write": 134225877},
+    "gate/dgrad_gemm": {"fetch": 4383752277, "write": 134227627},
+    "o/dgrad_gemm": {"fetch": 1278457813, "write": 134248832},
+    "v/dgrad_gemm": {"fetch": 191458091, "write": 134378880},
+    "k/dgrad_gemm": {"fetch": 191380181, "write": 134358997},
+    "q/dgrad_gemm": {"fetch": 1278411819, "write": 134246443},
 }
 
 
@@ -448,6 +466,29 @@ class LayerSet:
         return out
 
 
+def vendor_gemm(dev, layers, reps):
+    """Context for the fused GEMM's rate: the ROCm vendor library's plain bf16
+    GEMM (torch.matmul, no dequantization, no LoRA term) on the forward
+    shapes of the block's projections, beside the fused forward GEMM's time
+    from the per-layer pass.  Not part of the path and not a roofline."""
+    import torch
+    out = {"note": "torch.matmul on plain bf16 operands (x @ W^T, W already bf16); the fused kernel also "
+                   "dequantizes W and adds the LoRA term"}
+    for name, (M, m, n) in (("q", (8192, 8192, 8192)), ("gate", (8192, 28672, 8192)), ("down", (8192, 8192, 28672))):
+        a = torch.randn(M, n, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(m, n, device=dev, dtype=torch.bfloat16)
+        med, _ = timed_us(lambda: a @ w.t(), reps)
+        row = {"shape": f"M {M}, N {m}, K {n}", "us": round(med, 1),
+               "TFLOP/s": round(2 * M * m * n / (med * 1e-6) / 1e12, 1)}
+        fused = layers.get(name, {}).get("fwd_gemm")
+        if fused:
+            row["fused_fwd_gemm_us"] = fused["avg_us"]
+        out[name] = row
+        del a, w
+    torch.cuda.empty_cache()
+    return out
+
+
 def layer_passes(ls, reps):
     """Forward, backward and forward + backward of one layer (median of reps)."""
     d = ls.t[0]
@@ -587,6 +628,9 @@ def main():
         print(f"[bench] block passes done", file=sys.stderr, flush=True)
     del blk
     torch.cuda.empty_cache()
+    if not args.no_extra:
+        out["vendor_bf16_gemm"] = vendor_gemm(dev, layers, 10)
+        print(f"[bench] vendor GEMM context done", file=sys.stderr, flush=True)
 
     if not args.no_extra:
         gate = LayerSet(Q, dev, QI.WORKLOADS[2]["layers"], seed=2)

@@ -928,42 +928,70 @@ __global__ __launch_bounds__(256) void skinny_token_kernel(const uint16_t* __res
 // fp32 partials (stride M R, added in split order from 0, as
 // reduce_splits_kernel adds them) and, if Yout is given, also writes that
 // sum; grid y = 1 makes the planes P2 of a second factor Y2 (one part).  A
-// workgroup takes 64 tokens: their rows are staged in LDS, then every thread
-// writes 8 consecutive tokens of one plane row.
+// workgroup takes 8 tokens (8 R <= 1024 elements, up to 4 per thread) and
+// issues the loads of 4 splits of all its elements together, so a launch
+// waits for memory about ceil(nsplit / 4) times (with 64 tokens and one
+// element's splits at a time it waited 16 times: 15.8 us for the 70B
+// block's v at r = 64, 8 splits).  The sums are staged in LDS, then thread
+// i < 2 R writes the 8 tokens of plane row i (16 bytes).
+constexpr int kPlaneTok = 8;
 __global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restrict__ Y, int nsplit, int64_t M, int R,
                                                             int64_t Mp, uint16_t* __restrict__ P,
                                                             float* __restrict__ Yout, const float* __restrict__ Y2,
                                                             uint16_t* __restrict__ P2) {
-  __shared__ float sy[64][kMaxRank + 1];
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  __shared__ float sy[kPlaneTok][kMaxRank + 1];
+  const int64_t t0 = (int64_t)blockIdx.x * kPlaneTok;
   const bool second = blockIdx.y == 1;
   const float* src = second ? Y2 : Y;
   const int ns = second ? 1 : nsplit;
   uint16_t* dstp = second ? P2 : P;
-  for (int i = threadIdx.x; i < 64 * R; i += 256) {
-    const int t = i / R, q = i % R;
-    float acc = 0.0f;
-    if (t0 + t < M) {
-      const int64_t idx = (t0 + t) * R + q;
-      acc = sum_splits(src, ns, M * R, idx);
-      if (!second && Yout) Yout[idx] = acc;
+  const int64_t lim = M * R;
+  const int64_t base = t0 * R;
+  const int n = kPlaneTok * R;
+  constexpr int E = kPlaneTok * kMaxRank / 256;  // elements per thread at most
+  bool ok[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    ok[e] = i < n && base + i < lim;
+  }
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < ns; k0 += 4) {
+    float v[4][E];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        v[c][e] = (k0 + c < ns && ok[e]) ? src[(int64_t)(k0 + c) * lim + base + threadIdx.x + 256 * e] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (k0 + c < ns) acc[e] += v[c][e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = threadIdx.x + 256 * e;
+    if (i < n) {
+      sy[i / R][i % R] = acc[e];
+      if (!second && Yout && ok[e]) Yout[base + i] = acc[e];
     }
-    sy[t][q] = acc;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 2 * R * 8; i += 256) {
-    const int c = i & 7;
-    const int q = (i >> 3) % R;
-    const int pl = (i >> 3) / R;
+  if ((int)threadIdx.x < 2 * R) {
+    const int q = threadIdx.x % R;
+    const int pl = threadIdx.x / R;
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float h0, l0, h1, l1;
-      split_bf16(sy[8 * c + 2 * e][q], h0, l0);
-      split_bf16(sy[8 * c + 2 * e + 1][q], h1, l1);
+      split_bf16(sy[2 * e][q], h0, l0);
+      split_bf16(sy[2 * e + 1][q], h1, l1);
       w[e] = pl ? pack_bf16x2(l0, l1) : pack_bf16x2(h0, h1);
     }
-    *reinterpret_cast<u32x4*>(dstp + ((int64_t)pl * R + q) * Mp + t0 + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dstp + ((int64_t)pl * R + q) * Mp + t0) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -1045,7 +1073,7 @@ size_t token_planes_bytes(int64_t M, int R) { return (size_t)2 * R * (size_t)(cd
 void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t* P, float* Yout, const float* Y2,
                           uint16_t* P2, hipStream_t stream) {
   const int64_t Mp = cdiv(M, 64) * 64;
-  hipLaunchKernelGGL(factor_planes_kernel, dim3((unsigned)(Mp / 64), Y2 ? 2u : 1u), dim3(256), 0, stream, Y, nsplit,
+  hipLaunchKernelGGL(factor_planes_kernel, dim3((unsigned)(Mp / kPlaneTok), Y2 ? 2u : 1u), dim3(256), 0, stream, Y, nsplit,
                      M, R, Mp, P, Yout, Y2, P2);
 }
 
