@@ -324,35 +324,42 @@ def blas_threads():
         return None
 
 
-def cpu_baseline(cfg, layer, tokens):
+def cpu_baseline(cfg, layers, tokens):
     """Time the oracle (float64 numpy) on a bounded sample of the workload:
-    one layer's full quantization, then its forward and backward on a slice
-    of the tokens."""
+    for each of `layers` in turn, the whole weight's quantization and
+    dequantization, then its forward and backward on the first `tokens`
+    tokens (all of them by default)."""
     import qlora_inputs as QI
     from oracle import qlora_oracle as O
 
-    L = layer
-    inp = QI.layer_inputs(cfg, L, M=tokens)
-    t0 = time.perf_counter()
-    qw = O.quantize_nf4_dq(inp["W"])
-    Wd = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], L.m * L.n)).reshape(L.m, L.n)
-    x = O.bf16_bits_to_float64(inp["x"])
-    g = O.bf16_bits_to_float64(inp["g"])
-    A = O.bf16_bits_to_float64(inp["A"])
-    B = O.bf16_bits_to_float64(inp["B"])
-    h, u = O.linear_fwd(x, Wd, A, B, L.s)
-    O.linear_bwd(x, g, Wd, A, B, L.s, u=u)
-    dt = time.perf_counter() - t0
-    flops = fwd_flops(tokens, L.n, L.m, L.r) + bwd_flops(tokens, L.n, L.m, L.r)
+    dt = 0.0
+    flops = 0
+    for L in layers:
+        inp = QI.layer_inputs(cfg, L, M=tokens)
+        t0 = time.perf_counter()
+        qw = O.quantize_nf4_dq(inp["W"])
+        Wd = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], L.m * L.n)).reshape(L.m, L.n)
+        x = O.bf16_bits_to_float64(inp["x"])
+        g = O.bf16_bits_to_float64(inp["g"])
+        A = O.bf16_bits_to_float64(inp["A"])
+        B = O.bf16_bits_to_float64(inp["B"])
+        h, u = O.linear_fwd(x, Wd, A, B, L.s)
+        O.linear_bwd(x, g, Wd, A, B, L.s, u=u)
+        dt += time.perf_counter() - t0
+        flops += fwd_flops(tokens, L.n, L.m, L.r) + bwd_flops(tokens, L.n, L.m, L.r)
+        del inp, qw, Wd, x, g, A, B, h, u
     threads = blas_threads()
+    names = ", ".join(f"{L.name} {L.m}x{L.n}" for L in layers)
+    M = layers[0].M
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads) if threads else (os.cpu_count() or 1),
         "kind": "oracle",
-        "sample": (f"70B block, {L.name} projection {L.m}x{L.n}: quantize the whole weight, dequantize it, then "
-                   f"fwd + bwd for {tokens} of the {L.M} tokens, float64 numpy; {dt:.2f} s; "
-                   f"value = sample fwd+bwd flops / time (quantize and dequantize included)"),
+        "sample": (f"70B block, projections {names}: for each, quantize the whole weight, dequantize it, then " +
+                   (f"fwd + bwd of all {M} tokens" if tokens == M else f"fwd + bwd for {tokens} of the {M} tokens") +
+                   f", float64 numpy; {dt:.2f} s; value = sample fwd+bwd flops / time (quantize and dequantize "
+                   f"included)"),
         "blas_threads": threads,
         "os_cpu_count": os.cpu_count(),
         "seconds": round(dt, 2),
@@ -466,6 +473,57 @@ class LayerSet:
         return out
 
 
+def small_layer(Q, dev, reps):
+    """The 256 x 256 layer at 32 tokens (r = 8): absolute GPU times of the
+    quantizer, forward and backward (launch latency dominates, so no
+    roofline fraction), and the oracle's times for the same layer on the
+    host: float64 numpy (median of 5) and the pure-Python loop forward (one
+    run, one core)."""
+    import numpy as np
+    import torch
+    import qlora_inputs as QI
+    from oracle import qlora_oracle as O
+
+    L = QI.WORKLOADS[1]["layers"][0]
+    ls = LayerSet(Q, dev, [L], seed=1)
+    d = ls.t[0]
+    out = {"workload": f"single {L.m}x{L.n} layer, {L.M} tokens, r={L.r}, alpha={L.alpha:g}"}
+    for nm, fn in (("quantize", lambda: ls.quantize_one(d)), ("forward", lambda: ls.fwd_one(d)),
+                   ("backward", lambda: ls.bwd_one(d))):
+        med, mn = timed_us(fn, reps)
+        out[nm + "_us"] = round(med, 2)
+        out[nm + "_us_min"] = round(mn, 2)
+    del ls, d
+    inp = QI.layer_inputs(1, L)
+    x = O.bf16_bits_to_float64(inp["x"])
+    g = O.bf16_bits_to_float64(inp["g"])
+    A = O.bf16_bits_to_float64(inp["A"])
+    B = O.bf16_bits_to_float64(inp["B"])
+    ts = {"quantize": [], "forward": [], "backward": []}
+    for _ in range(5):
+        t0 = time.perf_counter()
+        qw = O.quantize_nf4_dq(inp["W"])
+        t1 = time.perf_counter()
+        Wd = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], L.m * L.n)).reshape(L.m, L.n)
+        t2 = time.perf_counter()
+        h, u = O.linear_fwd(x, Wd, A, B, L.s)
+        t3 = time.perf_counter()
+        O.linear_bwd(x, g, Wd, A, B, L.s, u=u)
+        t4 = time.perf_counter()
+        ts["quantize"].append(t1 - t0)
+        ts["forward"].append(t3 - t1)
+        ts["backward"].append(t4 - t3)
+    oracle = {k + "_us": round(float(np.median(v)) * 1e6, 1) for k, v in ts.items()}
+    t0 = time.perf_counter()
+    O.linear_fwd_loops(x, Wd, A, B, L.s)
+    oracle["forward_python_loops_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+    oracle["note"] = ("oracle on the host: float64 numpy, median of 5 (forward includes the dequantization); "
+                      "the loop forward is pure Python on one core")
+    out["oracle"] = oracle
+    torch.cuda.empty_cache()
+    return out
+
+
 def vendor_gemm(dev, layers, reps):
     """Context for the fused GEMM's rate: the ROCm vendor library's plain bf16
     GEMM (torch.matmul, no dequantization, no LoRA term) on the forward
@@ -519,7 +577,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--profile-reps", type=int, default=3, help="per-layer calls timed kernel by kernel")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the measurements outside the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -654,10 +712,11 @@ def main():
         out["adapter_adam"] = adapter_adam(Q, dev, 10)
         torch.cuda.empty_cache()
         out["small_tokens"] = small_token_block(Q, dev, 10)
+        out["small_layer"] = small_layer(Q, dev, 20)
         print(f"[bench] extras done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, QI.WORKLOADS[cfg]["layers"][0], args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, QI.WORKLOADS[cfg]["layers"][:4], args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

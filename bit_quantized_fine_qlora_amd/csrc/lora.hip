@@ -593,6 +593,47 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restric
   }
 }
 
+// The transposed case of reduce_grad_kernel (out [R][Jout]): thread (g, q)
+// sums rows j = 8 g .. 8 g + 7 at column q, each in split order from 0 as
+// sum_splits adds them, and writes the 8 results as 16 contiguous bytes of
+// out's row q.  A wave's loads of one row j are R consecutive floats, and
+// up to 16 loads of a thread are in flight together (one element per
+// thread wrote 2 bytes at stride Jout and waited for each element's loads).
+__global__ __launch_bounds__(256) void reduce_grad_t_kernel(const float* __restrict__ part, int nsplit, int64_t J,
+                                                            int64_t Jout, int R, float s,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t groups = (Jout + 7) / 8;
+  if (i >= groups * R) return;
+  const int q = (int)(i % R);
+  const int64_t j0 = (i / R) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < nsplit; k0 += 2) {
+    float v[2][8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[c][e] = (k0 + c < nsplit && j0 + e < Jout) ? part[(int64_t)(k0 + c) * J * R + (j0 + e) * R + q] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + c < nsplit) acc[e] += v[c][e];
+  }
+  uint16_t* dst = out + (int64_t)q * Jout + j0;
+  if ((Jout & 7) == 0) {
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(s * acc[0], s * acc[1]), pack_bf16x2(s * acc[2], s * acc[3]),
+                                           pack_bf16x2(s * acc[4], s * acc[5]), pack_bf16x2(s * acc[6], s * acc[7])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j0 + e < Jout) dst[e] = (uint16_t)(pack_bf16x2(s * acc[e], 0.f) & 0xFFFFu);
+  }
+}
+
 // out[r][0:cols] = in[r][0:cols], out[r][cols:cols_pad] = 0 (bf16 rows)
 __global__ __launch_bounds__(256) void pad_cols_bf16_kernel(const uint16_t* __restrict__ in, int64_t rows,
                                                             int64_t cols, int64_t cols_pad,
@@ -604,7 +645,10 @@ __global__ __launch_bounds__(256) void pad_cols_bf16_kernel(const uint16_t* __re
 }
 
 // out[c][r] = in[r][c] for a rows x cols bf16 matrix; out rows have length
-// ld >= rows and out[c][rows:ld] = 0.  One thread per output element.
+// ld >= rows and out[c][rows:ld] = 0.  One thread per output element (B^T
+// of a 70B layer, 28672 x 64: 10 us; a tile transpose through LDS was no
+// faster there and twice as slow on 1024 x 64, its load - barrier - store
+// chain being longer than the whole launch).
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t rows,
                                                              int64_t cols, int64_t ld, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1105,8 +1149,12 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
     }
   }
   const int64_t count = Jout * R;
-  hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
-                     Jout, R, s, transpose_out, out);
+  if (transpose_out)
+    hipLaunchKernelGGL(reduce_grad_t_kernel, dim3((unsigned)cdiv(cdiv(Jout, 8) * R, 256)), dim3(256), 0, stream,
+                       part, splits, J, Jout, R, s, out);
+  else
+    hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
+                       Jout, R, s, 0, out);
 }
 
 // The adapter part of grad_x under dropout, in fp32 for the grad_x GEMM to
