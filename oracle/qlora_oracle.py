@@ -657,6 +657,27 @@ def adapter_params(m: int, n: int, r: int) -> int:
 # [P4] Innovation 1 contrast NF4 with uniformly spaced INT4 levels)
 # --------------------------------------------------------------------------
 
+def int4_table():
+    """Return (Q, T) of symmetric INT4 absmax quantization as a 16-entry
+    table for the same pipeline: the 15 levels k/7, k = -7..7, with the zero
+    level written twice, as -0 (index 7) and +0 (index 8), so that the table
+    keeps the sign-magnitude symmetry Q_{15-j} = -Q_j bit for bit.
+    Q_{8+k} = fl32(k/7); T_j = fl32((Q_j + Q_{j+1}) / 2) as for NF4, which
+    makes T_7 = 0: a normalized weight w_hat > 0 takes +0 or above, w_hat <= 0
+    takes -0 or below, and both zeros dequantize to the value 0.  Apart from
+    fp32 rounding of the thresholds (and ties, which the threshold rule sends
+    to the lower level) the level of w_hat is rint(7 w_hat) / 7: the integer
+    absmax quantizer of int4_absmax_roundtrip, with double-quantized scales.
+    """
+    pos = np.array([k / 7.0 for k in range(8)], dtype=np.float64).astype(np.float32)
+    Q = np.concatenate([-pos[::-1], pos]).astype(np.float32)   # index 7 is -0.0
+    T = ((Q[:-1].astype(np.float64) + Q[1:].astype(np.float64)) / 2.0).astype(np.float32)
+    return Q, T
+
+
+INT4_Q, INT4_T = int4_table()
+
+
 def int4_absmax_roundtrip(W) -> np.ndarray:
     """Round trip through symmetric INT4 absmax quantization, blocks of 64.
 

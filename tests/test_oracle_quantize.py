@@ -309,6 +309,80 @@ def test_uniform4_error_above_nf4_and_near_int4():
     assert abs(errs["uniform4"] - e_int4) < 0.25 * e_int4
 
 
+# ------------------------------------------------------ INT4 absmax as a level table
+
+def test_int4_table_closed_form():
+    Q, T = O.int4_table()
+    for k in range(8):
+        assert Q[8 + k] == np.float32(k / 7.0)
+        assert Q[7 - k].view(np.uint32) == (-Q[8 + k]).view(np.uint32)   # bitwise, -0.0 included
+    assert Q[7] == 0.0 and np.signbit(Q[7]) and not np.signbit(Q[8])
+    assert np.all(np.diff(Q.astype(np.float64)) >= 0) and np.count_nonzero(np.diff(Q.astype(np.float64)) == 0) == 1
+    assert T[7] == 0.0
+    for j in range(15):
+        assert T[j] == np.float32((float(Q[j]) + float(Q[j + 1])) / 2.0)
+    for k in range(7):   # thresholds (2k + 1)/14 up to the two roundings (levels, then midpoint)
+        assert abs(float(T[8 + k]) - (2 * k + 1) / 14.0) <= 2.0 * float(np.spacing(T[8 + k]))
+
+
+def _int4_values(qw, n):
+    lev = O.unpack_codes(qw["codes"], n).astype(np.int64)   # level index 0..15
+    return O.INT4_Q.astype(np.float64)[lev]
+
+
+def test_int4_table_is_the_integer_absmax_quantizer():
+    # the threshold rule on the INT4 table picks k/7 with k = rint(7 w_hat),
+    # the textbook integer quantizer, except within one ulp of a threshold
+    rng = np.random.default_rng(21)
+    W = (rng.standard_normal((96, 512)) * 0.02).astype(np.float32)
+    W[3, :64] = 0.0                                    # an all-zero block: w_hat = 0 -> the zero level
+    qw = O.quantize_nf4_dq(W, table=O.int4_table())
+    got = np.rint(_int4_values(qw, W.size) * 7.0)          # fl32(k/7) * 7 rounds back to k
+    wb = W.reshape(-1, 64)
+    c1 = np.max(np.abs(wb), axis=1)
+    what = np.where(c1[:, None] > 0, wb / np.where(c1 > 0, c1, 1)[:, None], 0).astype(np.float32).reshape(-1)
+    k = np.rint(what.astype(np.float64) * 7.0)
+    diff = np.nonzero(got != k)[0]
+    for i in diff:
+        assert np.min(np.abs(O.INT4_T.astype(np.float64) - float(what[i]))) <= float(np.spacing(what[i]))
+    assert len(diff) <= 4
+    assert np.all(got[3 * 512:3 * 512 + 64] == 0.0)
+
+
+def test_int4_threshold_rule_equals_nearest_value():
+    # nearest level by brute force: the two zeros are one value, so compare
+    # values, not indices
+    rng = np.random.default_rng(22)
+    W = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    qw = O.quantize_nf4_dq(W, table=O.int4_table())
+    got = _int4_values(qw, W.size)
+    want = O.INT4_Q.astype(np.float64)[brute_nearest_codes(W, O.INT4_Q)]
+    diff = np.nonzero(got != want)[0]
+    wb = W.reshape(-1)
+    c1 = np.repeat(qw["c1"], 64)
+    for i in diff:
+        what = np.float32(wb[i]) / np.float32(c1[i])
+        assert np.min(np.abs(O.INT4_T.astype(np.float64) - float(what))) <= float(np.spacing(np.float32(what)))
+    assert len(diff) <= 2
+
+
+def test_int4_table_error_above_nf4_and_at_int4_roundtrip():
+    # through the same pipeline (double quant, bf16) INT4 loses to NF4 on
+    # normal weights, and sits at the exact-scale INT4 round trip
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+    w64 = W.reshape(-1).astype(np.float64)
+    rel = lambda a: np.linalg.norm(a - w64) / np.linalg.norm(w64)  # noqa: E731
+    errs = {}
+    for name, table in (("nf4", None), ("int4", O.int4_table())):
+        qw = O.quantize_nf4_dq(W, table=table)
+        deq = O.bf16_bits_to_float64(O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table))
+        errs[name] = rel(deq)
+    assert errs["nf4"] < errs["int4"]
+    e_exact = rel(O.int4_absmax_roundtrip(W))
+    assert abs(errs["int4"] - e_exact) < 0.05 * e_exact
+
+
 # ------------------------------------------------- edge-mean (quantile-average) table
 
 def _phi(x):
