@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     QTYPE_NF4,
     QTYPE_UNIFORM4,
     QTYPE_EDGE_MEAN4,
+    QTYPE_INT4,
     QuantizedWeight,
     AdamStep,
     adam_step,

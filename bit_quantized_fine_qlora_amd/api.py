@@ -54,6 +54,7 @@ def _need(t: torch.Tensor, dtype, shape, name: str):
 QTYPE_NF4 = 0
 QTYPE_UNIFORM4 = 1
 QTYPE_EDGE_MEAN4 = 2
+QTYPE_INT4 = 3
 
 
 def level_table(qtype: int = QTYPE_NF4):

@@ -111,6 +111,8 @@ double normal_quantile(double p) {
 //     level i is the mean of Phi^-1 at its bucket's edges i/16 and
 //     (i + 1)/16, with the two outermost edges (infinite quantiles) moved to
 //     the outer buckets' midpoints 1/32 and 31/32; normalized by the largest
+//   qtype 3 (INT4 absmax, "QLoRA: Efficient Fine-Tuning" Step 1): k/7 for
+//     k = -7..7, the zero level held twice, as -0 (index 7) and +0 (index 8)
 Nf4Table build_table(int qtype) {
   Nf4Table t;
   double q[16];
@@ -125,10 +127,13 @@ Nf4Table build_table(int qtype) {
     }
     for (int j = 0; j < 16; ++j) q[j] = 0.5 * (qe[j] + qe[j + 1]);
     for (int j = 0; j < 16; ++j) t.q[j] = (float)(q[j] / q[15]);
+  } else if (qtype == 3) {
+    for (int k = 0; k < 8; ++k) t.q[8 + k] = (float)(k / 7.0);
   } else {
     for (int j = 0; j < 16; ++j) t.q[j] = (float)((2.0 * j - 15.0) / 15.0);
   }
-  // exact symmetry of the construction, kept exact after rounding
+  // exact symmetry of the construction, kept exact after rounding (for the
+  // INT4 grid this writes -0 at index 7)
   for (int j = 0; j < 8; ++j) t.q[j] = -t.q[15 - j];
   for (int j = 0; j < 15; ++j) t.t[j] = (float)(((double)t.q[j] + (double)t.q[j + 1]) * 0.5);
   // The quantizer finds the code of |w/c1| through a table of eighth-binade
@@ -152,12 +157,15 @@ const Nf4Table& table(int qtype = 0) {
   if (qtype == 1) return u;
   static const Nf4Table e = build_table(2);
   if (qtype == 2) return e;
+  static const Nf4Table i4 = build_table(3);
+  if (qtype == 3) return i4;
   static const Nf4Table t = build_table(0);
   return t;
 }
 
 bool valid_qtype(int32_t qtype) {
-  return qtype == QLORA_QTYPE_NF4 || qtype == QLORA_QTYPE_UNIFORM4 || qtype == QLORA_QTYPE_EDGE_MEAN4;
+  return qtype == QLORA_QTYPE_NF4 || qtype == QLORA_QTYPE_UNIFORM4 || qtype == QLORA_QTYPE_EDGE_MEAN4 ||
+         qtype == QLORA_QTYPE_INT4;
 }
 
 // ---------------------------------------------------------------------------

@@ -166,6 +166,7 @@ qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, fl
 #define QLORA_QTYPE_NF4 0        /* the NF4 levels above */
 #define QLORA_QTYPE_UNIFORM4 1   /* uniform 4-bit grid (2j - 15)/15, j = 0..15 */
 #define QLORA_QTYPE_EDGE_MEAN4 2 /* mean of each bucket's edge quantiles (below) */
+#define QLORA_QTYPE_INT4 3       /* INT4 absmax grid k/7, k = -7..7 (below) */
 
 /*
  * The 16 levels and 15 thresholds of a level table (host outputs, either
@@ -179,8 +180,14 @@ qlora_status qlora_adam_step(const qlora_adam_tensor* tensors, int32_t count, fl
  * mean of the normal quantiles at its bucket's edges i/16 and (i + 1)/16;
  * as printed the outermost edges (probabilities 0 and 1) have infinite
  * quantiles, so they are moved to the outer buckets' midpoints 1/32 and
- * 31/32, and the levels are normalized by the largest.  QLORA_ERR_VALUE for
- * an unknown qtype.
+ * 31/32, and the levels are normalized by the largest.  QLORA_QTYPE_INT4 is
+ * symmetric 4-bit integer absmax quantization, the uniform comparison point
+ * those passages name: the 15 levels k/7, k = -7..7, with the zero level
+ * held twice, as -0 (index 7) and +0 (index 8), so that the table keeps the
+ * sign-magnitude symmetry of the code layout; the fp32 midpoint between
+ * them is 0, a normalized weight w_hat > 0 takes +0 or above and w_hat <= 0
+ * takes -0 or below, and both dequantize to the value 0.  QLORA_ERR_VALUE
+ * for an unknown qtype.
  */
 qlora_status qlora_level_table(int32_t qtype, float* levels, float* thresholds);
 

@@ -442,6 +442,37 @@ def test_edge_mean_quantizer(Q, m, n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("m,n", UNIFORM4)
+def test_int4_quantizer(Q, m, n):
+    # the INT4 absmax grid through the same kernels: bit-exact codes,
+    # constants and dequantized weight (both zeros included)
+    inp = QI.custom_inputs(seed=m + 5 * n, M=1, n=n, m=m, r=1)
+    W = inp["W"]
+    if m == 333:
+        W[7, :64] = 0.0            # an all-zero block: every weight takes the -0 level
+        W[9, 5] = 0.0              # an exact zero in a normal block
+    table = O.int4_table()
+    say(f"int4 quantize {m}x{n}")
+    q = Q.quantize_dq(torch.from_numpy(W).cuda(), qtype=Q.QTYPE_INT4)
+    torch.cuda.synchronize()
+    qw = O.quantize_nf4_dq(W, table=table)
+    check_quantizer(q, qw)
+    deq = host_bits(Q.dequant_dq(q, qtype=Q.QTYPE_INT4)).reshape(-1)
+    want = O.dequant_nf4_dq(qw["codes"], qw["absmax8"], qw["c2"], W.size, table=table)
+    assert np.array_equal(deq, want), "int4 dequantized weight differs"
+    if m * n >= 1 << 20:
+        # the pages' comparison with the GPU kernels: NF4 round trip beats INT4
+        w64 = W.reshape(-1).astype(np.float64)
+        qn = Q.quantize_dq(torch.from_numpy(W).cuda(), qtype=Q.QTYPE_NF4)
+        e_nf4 = np.linalg.norm(f64(host_bits(Q.dequant_dq(qn)).reshape(-1)) - w64) / np.linalg.norm(w64)
+        e_int4 = np.linalg.norm(f64(deq) - w64) / np.linalg.norm(w64)
+        say(f"round-trip rel-L2: nf4 {e_nf4:.5f}, int4 {e_int4:.5f}")
+        assert e_nf4 < e_int4
+        del qn
+    del q
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ adapter merge
 
 def bf16_order(bits):
