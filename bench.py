@@ -55,6 +55,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SPIN_CYCLES = 2_000_000   # torch.cuda._sleep before a timed call: ~1 ms at the shader clock
 BF16_PEAK_TFLOPS = 2500.0
 
 # HBM bytes per launch of the dominant GEMM kernels, from rocprofv3 --pmc
@@ -127,7 +128,11 @@ def small_forward_bytes(layers, M):
 
 
 def timed_us(fn, reps, flush=None):
-    """Median and min of `reps` event-timed calls of fn (after one untimed call)."""
+    """Median and min of `reps` event-timed calls of fn (after one untimed call).
+    The GPU is kept busy before the start event (by the flush read, or by a
+    spin kernel), so that the host has queued all of fn's launches before the
+    GPU reaches the start event: the time is the kernels', not the host's
+    launch gaps."""
     import torch
     fn()
     torch.cuda.synchronize()
@@ -135,6 +140,8 @@ def timed_us(fn, reps, flush=None):
     for _ in range(reps):
         if flush is not None:
             flush.sum()
+        else:
+            torch.cuda._sleep(SPIN_CYCLES)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -298,6 +305,7 @@ def dropout_passes(Q, x, g, q, A, B, s, h, u, out, ws_f, plain, reps):
     bwd_med, _ = timed_us(bwd, reps)
     Q.profile_enable(True)
     for _ in range(reps):
+        torch.cuda._sleep(SPIN_CYCLES)
         bwd()
     torch.cuda.synchronize()
     Q.profile_enable(False)
@@ -444,7 +452,9 @@ class LayerSet:
     def kernel_times(self, reps):
         """Per layer: average duration of every library kernel over `reps`
         forward + backward calls of that layer (HIP events on the launch
-        stream), the quantizer's too; checks that no K-split wait ran out."""
+        stream), the quantizer's too; checks that no K-split wait ran out.
+        A spin kernel ahead of each call keeps the host ahead of the GPU, so
+        that no event pair spans a gap in the host's launches."""
         import torch
         Q = self.Q
         out = {}
@@ -452,6 +462,7 @@ class LayerSet:
             L = d["L"]
             Q.profile_enable(True)
             for _ in range(reps):
+                torch.cuda._sleep(SPIN_CYCLES)
                 self.quantize_one(d)
                 self.fwd_one(d)
                 self.bwd_one(d)
@@ -548,6 +559,26 @@ def vendor_gemm(dev, layers, reps):
     return out
 
 
+def gate_sections(Q, dev, reps):
+    """The 8B gate projection (14336 x 4096, 4096 tokens, r = 16): forward,
+    backward and their kernels, the dropout passes, the adapter merge and the
+    level-table round trips."""
+    import torch
+    import qlora_inputs as QI
+    gate = LayerSet(Q, dev, QI.WORKLOADS[2]["layers"], seed=2)
+    out = {"gate_8B": layer_passes(gate, reps)}
+    d = gate.t[0]
+    L = d["L"]
+    out["gate_8B"]["kernels"] = gate.kernel_times(5)[L.name]
+    out["dropout"] = dropout_passes(Q, d["x"], d["g"], d["q"], d["A"], d["B"], L.s, d["h"], d["u"], d["out"],
+                                    gate.ws_f, out["gate_8B"], reps)
+    out["adapter_merge"] = adapter_merge(Q, d["q"], d["A"], d["B"], L.s, reps)
+    out["level_tables"] = level_table_variants(Q, d["W"], d["q"], reps)
+    del gate, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def layer_passes(ls, reps):
     """Forward, backward and forward + backward of one layer (median of reps)."""
     d = ls.t[0]
@@ -585,6 +616,8 @@ def main():
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--small-only", action="store_true",
                     help="only run the small-token section (for profiling it alone)")
+    ap.add_argument("--gate-only", action="store_true",
+                    help="only run the gate-projection sections (for profiling them alone)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -612,6 +645,9 @@ def main():
 
     if args.small_only:
         print(json.dumps({"small_tokens": small_token_block(Q, dev, max(args.steps, 3))}), flush=True)
+        return
+    if args.gate_only:
+        print(json.dumps(gate_sections(Q, dev, max(args.steps, 3))), flush=True)
         return
 
     cfg = 5
@@ -692,17 +728,7 @@ def main():
         print(f"[bench] vendor GEMM context done", file=sys.stderr, flush=True)
 
     if not args.no_extra:
-        gate = LayerSet(Q, dev, QI.WORKLOADS[2]["layers"], seed=2)
-        out["gate_8B"] = layer_passes(gate, 10)
-        d = gate.t[0]
-        L = d["L"]
-        out["gate_8B"]["kernels"] = gate.kernel_times(5)[L.name]
-        out["dropout"] = dropout_passes(Q, d["x"], d["g"], d["q"], d["A"], d["B"], L.s, d["h"], d["u"], d["out"],
-                                        gate.ws_f, out["gate_8B"], 10)
-        out["adapter_merge"] = adapter_merge(Q, d["q"], d["A"], d["B"], L.s, 10)
-        out["level_tables"] = level_table_variants(Q, d["W"], d["q"], 10)
-        del gate, d
-        torch.cuda.empty_cache()
+        out.update(gate_sections(Q, dev, 10))
         print(f"[bench] gate projection done", file=sys.stderr, flush=True)
         down = LayerSet(Q, dev, QI.WORKLOADS[3]["layers"], seed=3)
         out["down_8B"] = layer_passes(down, 10)
