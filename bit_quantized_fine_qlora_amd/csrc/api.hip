@@ -178,6 +178,9 @@ struct Rec {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<Rec> g_recs;
+// Set while qlora_linear_fwd_static runs on this thread: it records no
+// events (creating them and growing the record list would allocate).
+thread_local bool t_prof_suppressed = false;
 
 struct Timed {
   hipStream_t s;
@@ -186,7 +189,7 @@ struct Timed {
   bool on;
   Timed(const char* nm, hipStream_t st) : s(st), name(nm) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    on = g_prof_on;
+    on = g_prof_on && !t_prof_suppressed;
     if (on) {
       hipEventCreate(&a);
       hipEventCreate(&b);
@@ -599,6 +602,10 @@ qlora_status qlora_linear_fwd_static(int64_t M, int64_t n, int64_t m, int32_t r,
   DropoutDev dd;
   float inv_keep;
   make_dropout(nullptr, dd, inv_keep);
+  struct NoProfile {
+    NoProfile() { t_prof_suppressed = true; }
+    ~NoProfile() { t_prof_suppressed = false; }
+  } no_profile;
   return run_fwd(M, n, m, r, s, x, codes, absmax8, c2, A, B, h, u_out, dd, inv_keep, w, use_ksplit, ws,
                  reinterpret_cast<hipStream_t>(stream));
 }

@@ -246,7 +246,9 @@ qlora_status qlora_linear_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float 
  * qlora_linear_fwd (with a workspace of qlora_workspace_bytes(0, ...) the
  * two give identical bits).  The scratch is a library-owned device array of
  * QLORA_STATIC_SCRATCH_BYTES per device, held until the process ends; the
- * call allocates and frees nothing.  When the forward's workspace layout is
+ * call allocates and frees nothing (with library profiling switched on it
+ * records no events: qlora_profile_query does not see it).  When the
+ * forward's workspace layout is
  * larger than that array, the call runs its GEMM without the K-split region
  * (every output tile whole: same results up to fp32 summation order) if the
  * rest fits, and otherwise returns QLORA_ERR_WORKSPACE before launching

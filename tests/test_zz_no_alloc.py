@@ -87,3 +87,27 @@ def test_static_forward_layout_larger_than_scratch(Q):
     assert not run_pair(Q, M, n, m, r, 2.0, seed=14, oracle=False)
     # and a smaller call after it, back on the full layout
     assert run_pair(Q, 64, 1024, 1500, 32, 1.0, seed=15)
+
+
+def test_static_forward_records_no_events(Q):
+    # with library profiling switched on, the allocation-free call records no
+    # events (creating them would allocate); the workspace call still does
+    M, n, m, r = 512, 1024, 1024, 16
+    inp, q, x, A, B = layer(Q, M, n, m, r, seed=21)
+    h = torch.empty((M, m), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r), 256), dtype=torch.uint8, device="cuda")
+    say("static forward with profiling on")
+    Q.profile_enable(True)
+    try:
+        Q.linear_fwd_static(x, q, A, B, 2.0, h, u)
+        torch.cuda.synchronize()
+        assert Q.profile_query("fwd_gemm") == (0, 0.0)
+        assert Q.profile_query("down_proj") == (0, 0.0)
+        Q.linear_fwd(x, q, A, B, 2.0, h=h, u=u, workspace=ws)
+        torch.cuda.synchronize()
+        assert Q.profile_query("fwd_gemm")[0] == 1
+    finally:
+        Q.profile_enable(False)
+    ref = oracle_full(inp["W"], inp["x"], None, inp["A"], inp["B"], 2.0)
+    assert_close(f64(host_bits(h)), ref["h"], "h")
