@@ -137,8 +137,9 @@ Nf4Table build_table(int qtype) {
   for (int j = 0; j < 8; ++j) t.q[j] = -t.q[15 - j];
   for (int j = 0; j < 15; ++j) t.t[j] = (float)(((double)t.q[j] + (double)t.q[j + 1]) * 0.5);
   // The quantizer finds the code of |w/c1| through a table of eighth-binade
-  // intervals of [2^-4, 1] that may hold at most one positive threshold each
-  // (and none below 2^-4); these thresholds satisfy that, checked here once.
+  // intervals of [0, 1] that may hold at most one positive threshold each;
+  // checked here once (with every threshold at or above 2^-4, which all the
+  // tables here satisfy).
   uint32_t prev = 0;
   for (int j = 8; j < 15; ++j) {
     uint32_t b;

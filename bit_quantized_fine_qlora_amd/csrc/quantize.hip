@@ -26,27 +26,26 @@ __device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) 
 // non-negative floats order like the floats):
 //   v > 0 : level 8 + #{T_j < v}        -> code #{T_j < |v|}
 //   v <= 0: level 7 - #{T_j <= |v|}     -> code 8 + #{T_j < succ(|v|)}
-// (succ(|v|) is |v|'s bit pattern + 1; -0 and +0 both give level 7).
+// (succ(|v|) is |v|'s bit pattern + 1).  v <= 0 is read off the sign bit, so
+// a zero quotient must arrive as -0 (both zeros take level 7, like any v <= 0
+// with |v| below the first positive threshold).
 //
-// The count uses a 33-entry table over |v| in [2^-4, 1]: entry i covers the
-// bit patterns [2^-4 bits + i * 2^20, + 2^20) (an eighth of a binade) and
-// holds the number of thresholds below its start and the one threshold
-// inside it, if any (no interval holds two; the host-side table build checks
-// this).  |v| < 2^-4 lies below every threshold (entry 0 is empty) and
-// |v| = 1 is entry 32.  The key succ(|v|) may fall in the next interval, but
-// only at its very first pattern, which no threshold of the current entry
-// can reach, so base + [key > thr] is still the count.
-constexpr int kCodeLutSize = 33;
-constexpr uint32_t kCodeLutLo = 0x3D800000u;   // bit pattern of 2^-4
+// The count uses a 1024-entry table over the bit patterns of |v| in [0, 1]:
+// entry i covers the patterns [i * 2^20, (i + 1) * 2^20) (an eighth of a
+// binade) and holds the number of thresholds below its start and the one
+// threshold inside it, if any (no interval holds two, and none lies below
+// 2^-4; the host-side table build checks both).  The index is bits 20..29 of
+// v (|v| = 1 is entry 1016), so the lookup needs no clamp.  The key succ(|v|)
+// may fall in the next interval, but only at its very first pattern, which
+// no threshold of the current entry can reach, so base + [key > thr] is
+// still the count.
+constexpr int kCodeLutSize = 1024;
 
 __device__ __forceinline__ uint32_t nf4_code(float v, const uint2* lut) {
   const uint32_t bits = __float_as_uint(v);
-  const uint32_t abits = bits & 0x7FFFFFFFu;
-  const uint32_t neg = ((int32_t)bits <= 0) ? 1u : 0u;
-  const uint32_t key = abits + neg;
-  int idx = (int)(abits >> 20) - (int)(kCodeLutLo >> 20);
-  idx = idx < 0 ? 0 : (idx > kCodeLutSize - 1 ? kCodeLutSize - 1 : idx);
-  const uint2 e = lut[idx];
+  const uint32_t neg = bits >> 31;
+  const uint32_t key = (bits & 0x7FFFFFFFu) + neg;
+  const uint2 e = lut[(bits >> 20) & (kCodeLutSize - 1)];
   return (e.x + (key > e.y ? 1u : 0u)) | (neg << 3);
 }
 
@@ -63,8 +62,8 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
   const int tid = threadIdx.x;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
   const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
-  if (tid < kCodeLutSize) {
-    const uint32_t lo = kCodeLutLo + ((uint32_t)tid << 20);
+  for (int i = tid; i < kCodeLutSize; i += 256) {
+    const uint32_t lo = (uint32_t)i << 20;
     const uint32_t hi = lo + (1u << 20);
     uint32_t below = 0, inside = 0xFFFFFFFFu;
 #pragma unroll
@@ -73,7 +72,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
       below += t < lo ? 1u : 0u;
       if (t >= lo && t < hi) inside = t;
     }
-    s_lut[tid] = make_uint2(below, inside);
+    s_lut[i] = make_uint2(below, inside);
   }
   __syncthreads();
 
@@ -112,12 +111,15 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
     const float c1 = a;
     if (valid && quarter == 0) s_c1[lb] = c1;
 
-    // Fast path needs every quotient away from underflow; anything else
-    // (zeros, tiny or huge constants) takes the IEEE division.
+    // Fast path needs every quotient away from underflow (the division's
+    // residual is exact for |w| >= 2^-100 and c1 in [2^-100, 2^100], and
+    // |w| >= c1 2^-125 keeps w / c1 a normal number, never 0); anything else
+    // (zeros, tiny weights, tiny or huge constants) takes the IEEE division,
+    // and a zero quotient there is passed on as -0 (see nf4_code).
     float amin = fabsf(w[0]);
 #pragma unroll
     for (int i = 1; i < 16; ++i) amin = fminf(amin, fabsf(w[i]));
-    const bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f) || !(amin >= 0x1p-100f);
+    const bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f) || !(amin >= 0x1p-100f) || !(amin >= c1 * 0x1p-125f);
     float q[16];
     if (!slow) {
       const float y = 1.0f / c1;
@@ -125,7 +127,10 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
       for (int i = 0; i < 16; ++i) q[i] = div_by_block_absmax(w[i], c1, y);
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        const float v = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
+        q[i] = v == 0.0f ? -0.0f : v;
+      }
     }
     // pack: per 8 weights, byte j = code(w_j) | code(w_{j+4}) << 4
     uint32_t lo = 0, hi = 0;
