@@ -640,28 +640,17 @@ int device_cus() {
   return cached[dev];
 }
 
-// Tiles whose last round would leave at least half of the CUs idle are split
-// in K: with T tiles on C CUs (one workgroup per CU), the last T mod C <= C/2
-// tiles become 2 (T mod C) half-length work items, so the last round fills
-// the chip for half the time instead of half the chip for the full time.
-int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT);
-  const int cus = device_cus();
-  const int64_t rem = tiles % cus;
-  const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
-  if (nk < 8) return 0;
-  if (tiles < cus || rem == 0 || rem > cus / 2) return 0;
-  return (int)rem;
-}
-
 // Few tiles (at most half the CUs, e.g. 33..256 tokens at 4096 - 14336
 // features): every tile runs as P K pieces, P = min(CUs / tiles, 16) with
-// at least 8 K steps per piece, so up to all CUs stream the weight.  The P
-// fp32 tile sums (tiles P 2^18 <= CUs 2^18 bytes) are added in piece order
-// by a separate pass, so the result does not depend on which piece ends first.
+// at least 8 K steps per piece, so up to all CUs stream the weight.  With
+// P >= 3 the P fp32 tile sums (tiles P 2^18 <= CUs 2^18 bytes) are added in
+// piece order by a separate pass, so the result does not depend on which
+// piece ends first.  With P = 2 the two halves meet through the K-split
+// hand-off instead (commutative, so also order-free): no second pass, and
+// half the fp32 traffic (the 70B block's k and v forwards: 128 tiles).
 constexpr int kMaxPieces = 16;
 static int64_t tiles_of(int64_t M, int64_t N) { return ((N + lg2::BF - 1) / lg2::BF) * ((M + lg2::BT - 1) / lg2::BT); }
-int gemm_pieces(int64_t M, int64_t N, int64_t K) {
+static int few_tile_pieces(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = tiles_of(M, N);
   const int cus = device_cus();
   const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
@@ -670,6 +659,28 @@ int gemm_pieces(int64_t M, int64_t N, int64_t K) {
   if (pc > kMaxPieces) pc = kMaxPieces;
   while (pc > 1 && nk / pc < 8) --pc;
   return (int)pc;
+}
+int gemm_pieces(int64_t M, int64_t N, int64_t K) {
+  const int pc = few_tile_pieces(M, N, K);
+  return pc == 2 ? 1 : pc;
+}
+
+// Tiles split in two K halves that meet through the hand-off: every tile
+// when the few-tile mode would use two pieces; otherwise, when the tile
+// count leaves at most half a round for the last pass, those last tiles:
+// with T tiles on C CUs (one workgroup per CU), the last T mod C <= C/2
+// tiles become 2 (T mod C) half-length work items, so the last round fills
+// the chip for half the time instead of half the chip for the full time.
+// Either way the two halves of a tile run in the same round.
+int gemm_split_tiles(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = tiles_of(M, N);
+  const int cus = device_cus();
+  const int64_t rem = tiles % cus;
+  const int64_t nk = (K + lg2::BK - 1) / lg2::BK;
+  if (nk < 8) return 0;
+  if (tiles * 2 <= cus) return few_tile_pieces(M, N, K) == 2 ? (int)tiles : 0;
+  if (tiles < cus || rem == 0 || rem > cus / 2) return 0;
+  return (int)rem;
 }
 
 // Finishes a few-tile GEMM: out = bf16(((piece 0 + piece 1) + ...) + add).

@@ -160,7 +160,6 @@ def test_linear_check_without_hand_off(lib):
     # nothing read back (no GPU is touched); bad arguments are rejected first
     f = lib.qlora_linear_check
     assert f(0, 16, 4096, 1024, 16, None, None) == 0       # weight-streaming forward
-    assert f(1, 16, 4096, 1024, 16, None, None) == 0       # 16 grad_x tiles: K pieces, no wait
     assert f(0, 4096, 4096, 4096, 16, None, None) == 0     # 256 tiles: one full round
     assert f(1, 256, 4096, 14336, 16, None, None) == 0     # few tiles: K pieces, no wait
     assert f(3, 4096, 4096, 4096, 16, None, None) == -7    # unknown op
@@ -168,6 +167,8 @@ def test_linear_check_without_hand_off(lib):
     assert f(0, 4096, 4096, 4096, 0, None, None) == -3     # r = 0
     # this grad_x GEMM (896 tiles) splits its last round: the workspace is needed
     assert f(1, 4096, 14336, 4096, 16, None, None) == -1
+    # 16 grad_x tiles over K = 1024 run as two K halves through the hand-off
+    assert f(1, 16, 4096, 1024, 16, None, None) == -1
 
 
 def test_static_forward_rejects_large_layouts(lib):

@@ -168,7 +168,8 @@ FEW_TILES = [
     # CUs: every tile runs as P K pieces whose fp32 planes a second pass adds
     # in piece order.  P (forward / grad_x on 256 CUs): 4 / 5 with ragged
     # features (m % 4 != 0, M m odd); 4 / 9 with two LoRA steps in the last
-    # piece; 2 / 16; 8 / 1 (too few K steps to split the grad_x GEMM).
+    # piece; 2 / 16 (P = 2: two halves through the K-split hand-off); 8 / 1
+    # (too few K steps to split the grad_x GEMM).
     (200, 2048, 3001, 16, 2.0),
     (96, 2048, 5000, 40, 0.5),
     (256, 1024, 8192, 8, 1.0),
@@ -179,7 +180,8 @@ FEW_TILES = [
 def expected_pieces(M, N, K, cus):
     """K pieces per output tile of the few-tile mode: P = min(CUs / tiles, 16)
     when the tiles fill at most half the CUs, lowered until every piece keeps
-    at least 8 K steps of 64."""
+    at least 8 K steps of 64.  P = 2 runs as two halves through the K-split
+    hand-off (one fp32 plane per tile), P >= 3 as pieces (P planes a tile)."""
     tiles = -(-M // 256) * -(-N // 256)
     if tiles * 2 > cus:
         return 1, tiles
@@ -190,6 +192,11 @@ def expected_pieces(M, N, K, cus):
     return pc, tiles
 
 
+def few_tile_planes(pc):
+    """fp32 256 x 256 planes per tile in the workspace of a few-tile GEMM."""
+    return 1 if pc == 2 else pc
+
+
 @pytest.mark.parametrize("M,n,m,r,s", FEW_TILES)
 def test_k_pieces_few_tiles(Q, M, n, m, r, s):
     lib = Q._lib.load()
@@ -198,19 +205,27 @@ def test_k_pieces_few_tiles(Q, M, n, m, r, s):
     pb, tb = expected_pieces(M, n, m, cus)      # grad_x: N = n, K = m
     if pf == 1 and pb == 1:
         pytest.skip(f"{tf} / {tb} tiles on {cus} CUs: neither GEMM runs in K pieces")
-    # each GEMM that runs in pieces keeps P fp32 planes of 256 x 256 per tile in its workspace
+    # each GEMM that runs in pieces keeps P fp32 planes of 256 x 256 per tile
+    # in its workspace (one per tile when the two halves meet by hand-off)
     if pf > 1:
-        assert lib.qlora_workspace_bytes(0, M, n, m, r) >= pf * tf * 256 * 256 * 4, "forward K-piece planes missing"
+        assert lib.qlora_workspace_bytes(0, M, n, m, r) >= few_tile_planes(pf) * tf * 256 * 256 * 4, \
+            "forward K-piece planes missing"
     if pb > 1:
-        assert lib.qlora_workspace_bytes(1, M, n, m, r) >= pb * tb * 256 * 256 * 4, "grad_x K-piece planes missing"
+        assert lib.qlora_workspace_bytes(1, M, n, m, r) >= few_tile_planes(pb) * tb * 256 * 256 * 4, \
+            "grad_x K-piece planes missing"
     say(f"k-pieces: forward P={pf} ({tf} tiles), grad_x P={pb} ({tb} tiles)")
     inp = QI.custom_inputs(seed=7 * M + m + 11 * r, M=M, n=n, m=m, r=r)
     got, _ = check_full(Q, inp["W"], inp, s, label=f"k-pieces M={M} n={n} m={m} r={r}")
     say("k-pieces determinism")
+    ws_f = torch.empty(Q.workspace_bytes(Q.QLORA_OP_FWD, M, n, m, r), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(Q.workspace_bytes(Q.QLORA_OP_BWD, M, n, m, r), dtype=torch.uint8, device="cuda")
     for _ in range(2):
-        h2, u2 = Q.linear_fwd(got["x"], got["q"], got["A"], got["B"], s)
-        gx2, gA2, gB2 = Q.linear_bwd(got["x"], got["g"], got["q"], got["A"], got["B"], s, u=u2)
+        h2, u2 = Q.linear_fwd(got["x"], got["q"], got["A"], got["B"], s, workspace=ws_f)
+        gx2, gA2, gB2 = Q.linear_bwd(got["x"], got["g"], got["q"], got["A"], got["B"], s, u=u2, workspace=ws_b)
         torch.cuda.synchronize()
+        # two-half GEMMs: no hand-off wait ran out
+        Q.linear_check(Q.QLORA_OP_FWD, M, n, m, r, ws_f)
+        Q.linear_check(Q.QLORA_OP_BWD, M, n, m, r, ws_b)
         assert torch.equal(h2, got["h"]) and torch.equal(u2, got["u"])
         assert torch.equal(gx2, got["grad_x"]) and torch.equal(gA2, got["grad_A"]) and torch.equal(gB2, got["grad_B"])
 
