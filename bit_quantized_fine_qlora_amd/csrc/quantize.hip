@@ -25,124 +25,169 @@ __device__ __forceinline__ float div_by_block_absmax(float w, float c, float y) 
 // |v| against the 7 positive thresholds, as integers (bit patterns of
 // non-negative floats order like the floats):
 //   v > 0 : level 8 + #{T_j < v}        -> code #{T_j < |v|}
-//   v <= 0: level 7 - #{T_j <= |v|}     -> code 8 + #{T_j < succ(|v|)}
-// (succ(|v|) is |v|'s bit pattern + 1).  v <= 0 is read off the sign bit, so
-// a zero quotient must arrive as -0 (both zeros take level 7, like any v <= 0
-// with |v| below the first positive threshold).
+//   v <= 0: level 7 - #{T_j <= |v|}     -> code 8 + #{T_j <= |v|}
+// v <= 0 is read off the sign bit, so a zero quotient must arrive as -0
+// (both zeros take level 7, like any v <= 0 with |v| below the first
+// positive threshold).
 //
-// The count uses a 1024-entry table over the bit patterns of |v| in [0, 1]:
-// entry i covers the patterns [i * 2^20, (i + 1) * 2^20) (an eighth of a
-// binade) and holds the number of thresholds below its start and the one
-// threshold inside it, if any (no interval holds two, and none lies below
-// 2^-4; the host-side table build checks both).  The index is bits 20..29 of
-// v (|v| = 1 is entry 1016), so the lookup needs no clamp.  The key succ(|v|)
-// may fall in the next interval, but only at its very first pattern, which
-// no threshold of the current entry can reach, so base + [key > thr] is
-// still the count.
-constexpr int kCodeLutSize = 1024;
+// The count uses a table over the bit patterns of v in [-1, 1], in two
+// halves by the sign bit.  Entry i of a half covers the |v| patterns
+// [i * 2^20, (i + 1) * 2^20) (an eighth of a binade) and holds the code of
+// the interval's start and the one threshold inside it, if any (no interval
+// holds two, and none lies below 2^-4; the host-side table build checks
+// both), as the full bit pattern above which v takes the next code: T for
+// v > 0, and sign | (T - 1) for v <= 0, so that one unsigned compare of v's
+// own bits gives T < |v| or T <= |v| respectively.  The byte offset of the
+// entry is bits 17..29 and 31 of v masked to 8-byte steps: bit 31 selects
+// the half (16 KB apart), and bit 30 is 0 for |v| <= 1 (|v| = 1 is entry
+// 1016), so the lookup needs no clamp.
+constexpr int kCodeLutSize = 1024;              // entries per sign
+constexpr int kCodeLutFirst = 0x3D800000 >> 20; // the entry of 2^-4
+constexpr uint32_t kCodeLutMask = 0x5FF8u;      // (bits >> 17) & mask = byte offset
+constexpr int kCodeLutNegBase = 2048;           // first entry of the v <= 0 half
 
 __device__ __forceinline__ uint32_t nf4_code(float v, const uint2* lut) {
   const uint32_t bits = __float_as_uint(v);
-  const uint32_t neg = bits >> 31;
-  const uint32_t key = (bits & 0x7FFFFFFFu) + neg;
-  const uint2 e = lut[(bits >> 20) & (kCodeLutSize - 1)];
-  return (e.x + (key > e.y ? 1u : 0u)) | (neg << 3);
+  const uint2 e = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lut) + ((bits >> 17) & kCodeLutMask));
+  return e.x + (bits > e.y ? 1u : 0u);
 }
 
-// One workgroup per double-quant group (256 blocks of 64 weights).  In each
-// of four passes a quad of lanes covers one block, 16 consecutive weights per
-// lane (four 16-byte loads), so a wave reads 4 KB of contiguous weights.
+// Maximum over the 8 lanes 8k .. 8k + 7 by three DPP butterfly steps
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror).
+__device__ __forceinline__ float oct_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xF, 0xF, false)));
+  return a;
+}
+
+// v | (the same value of the neighbouring lane, lane ^ 1).
+__device__ __forceinline__ uint32_t or_lane_pair(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// q = fl32(w / c1) for 8 weights of one block.  The fast path needs every
+// quotient away from underflow (the division's residual is exact for
+// |w| >= 2^-100 and c1 in [2^-100, 2^100], and |w| >= c1 2^-125 keeps w / c1
+// a normal number, never 0); anything else (zeros, tiny weights, tiny or huge
+// constants) takes the IEEE division, and a zero quotient there is passed on
+// as -0 (see nf4_code).  The choice is per lane: both paths give the same
+// quotients where both apply.
+__device__ __forceinline__ void block_quotients(const float* w, float c1, float* q) {
+  float amin = fabsf(w[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) amin = fminf(amin, fabsf(w[i]));
+  const bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f) || !(amin >= 0x1p-100f) || !(amin >= c1 * 0x1p-125f);
+  if (!slow) {
+    const float y = 1.0f / c1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = div_by_block_absmax(w[i], c1, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
+      q[i] = v == 0.0f ? -0.0f : v;
+    }
+  }
+}
+
+constexpr int kAuxNonTemporal = 2;  // buffer access cache policy: nt
+
+// One workgroup per double-quant group (256 blocks of 64 weights), in four
+// passes of 64 blocks.  Per pass each wave takes 16 consecutive blocks (4 KB),
+// 8 lanes to a pair of blocks: lane t of lane octet g reads the 16 bytes at
+// t * 16 of each 128-byte half of blocks 2g and 2g + 1, so every 16-byte load
+// of the wave covers eight whole 128-byte lines, and each lane holds 8
+// weights of each of its two blocks (weights 4t .. 4t + 3 and 32 + 4t ..
+// 32 + 4t + 3).  The loads are non-temporal (the weight is read once) and
+// go through buffer resources with the group's byte range, so the partial
+// last group reads zeros and drops its stores past the end.  Block maxima come
+// from DPP steps over the octet; the 4 codes of a lane's 4 consecutive
+// weights fill one nibble of each byte of a code word and the neighbouring
+// lane the other (weights 8p .. 8p + 3 low, 8p + 4 .. 8p + 7 high), merged
+// by one DPP exchange; even lanes store the first block's words, odd lanes
+// the second's.
 __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ W, int64_t nblk,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ absmax8,
                                                                float* __restrict__ c2out, Nf4Table tab) {
-  __shared__ float s_c1[kGroupBlocks];
-  __shared__ float s_red[4];
-  __shared__ uint2 s_lut[kCodeLutSize];
+  // code table (both halves) with the block constants and the group
+  // maximum in the gap between the halves
+  __shared__ uint2 s_lut[kCodeLutNegBase + kCodeLutSize];
+  float* s_c1 = reinterpret_cast<float*>(s_lut + kCodeLutSize);
+  float* s_red = s_c1 + kGroupBlocks;
   const int tid = threadIdx.x;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
   const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
-  for (int i = tid; i < kCodeLutSize; i += 256) {
-    const uint32_t lo = (uint32_t)i << 20;
-    const uint32_t hi = lo + (1u << 20);
-    uint32_t below = 0, inside = 0xFFFFFFFFu;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int oct = lane >> 3, t = lane & 7;
+  const brsrc_t wr = make_rsrc(W + blk0 * kBlock, (uint32_t)nb * kBlock * 4u);
+  const brsrc_t cr = make_rsrc(codes + blk0 * (kBlock / 2), (uint32_t)nb * (kBlock / 2));
+  auto load_pass = [&](int pass, u32x4 (&dst)[4]) {
+    const uint32_t base = (uint32_t)(pass * 64 + wave * 16 + oct * 2) * kBlock * 4u + (uint32_t)t * 16u;
 #pragma unroll
-    for (int j = 0; j < 7; ++j) {
-      const uint32_t t = __float_as_uint(tab.t[8 + j]);
-      below += t < lo ? 1u : 0u;
-      if (t >= lo && t < hi) inside = t;
+    for (int k = 0; k < 4; ++k)
+      dst[k] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(base + (uint32_t)k * 128u), 0, kAuxNonTemporal));
+  };
+  // the first pass's loads are in flight while the table is built; the
+  // next pass's are issued before each pass's arithmetic
+  u32x4 wq[2][4];
+  load_pass(0, wq[0]);
+  for (int i = tid; i < kCodeLutSize; i += 256) {
+    uint32_t below = 0, inside = 0xFFFFFFFFu;
+    if (i >= kCodeLutFirst) {  // below 2^-4: no threshold below or inside
+      const uint32_t lo = (uint32_t)i << 20;
+      const uint32_t hi = lo + (1u << 20);
+#pragma unroll
+      for (int j = 0; j < 7; ++j) {
+        const uint32_t th = __float_as_uint(tab.t[8 + j]);
+        below += th < lo ? 1u : 0u;
+        if (th >= lo && th < hi) inside = th;
+      }
     }
     s_lut[i] = make_uint2(below, inside);
+    s_lut[kCodeLutNegBase + i] = make_uint2(8u + below, inside == 0xFFFFFFFFu ? inside : (0x80000000u | (inside - 1u)));
   }
   __syncthreads();
 
-  // The next pass's 64 bytes per lane are loaded before this pass's
-  // arithmetic, so each lane keeps two passes of loads in flight.
-  float4 wq[2][4];
-  auto load_pass = [&](int pass, float4 (&dst)[4]) {
-    const int lb = pass * 64 + (tid >> 2);
-    if (lb < nb) {
-      const float4* src = reinterpret_cast<const float4*>(W + (blk0 + lb) * kBlock + (tid & 3) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  load_pass(0, wq[0]);
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
-    const int lb = pass * 64 + (tid >> 2);
-    const int quarter = tid & 3;
-    const bool valid = lb < nb;
     if (pass + 1 < 4) load_pass(pass + 1, wq[(pass + 1) & 1]);
+    const int lb = pass * 64 + wave * 16 + oct * 2;  // first of the octet's two blocks
+    // w[0..7]: block lb, w[8..15]: block lb + 1
     float w[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 t = wq[pass & 1][i];
-      w[4 * i + 0] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * k + e] = __uint_as_float(wq[pass & 1][k][e]);
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a0 = fmaxf(a0, fabsf(w[i]));
+      a1 = fmaxf(a1, fabsf(w[8 + i]));
     }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
-    a = fmaxf(a, __shfl_xor(a, 1));
-    a = fmaxf(a, __shfl_xor(a, 2));
-    const float c1 = a;
-    if (valid && quarter == 0) s_c1[lb] = c1;
-
-    // Fast path needs every quotient away from underflow (the division's
-    // residual is exact for |w| >= 2^-100 and c1 in [2^-100, 2^100], and
-    // |w| >= c1 2^-125 keeps w / c1 a normal number, never 0); anything else
-    // (zeros, tiny weights, tiny or huge constants) takes the IEEE division,
-    // and a zero quotient there is passed on as -0 (see nf4_code).
-    float amin = fabsf(w[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) amin = fminf(amin, fabsf(w[i]));
-    const bool slow = !(c1 >= 0x1p-100f && c1 <= 0x1p100f) || !(amin >= 0x1p-100f) || !(amin >= c1 * 0x1p-125f);
+    a0 = oct_max(a0);
+    a1 = oct_max(a1);
+    if (t == 0 && lb < nb) s_c1[lb] = a0;
+    if (t == 1 && lb + 1 < nb) s_c1[lb + 1] = a1;
     float q[16];
-    if (!slow) {
-      const float y = 1.0f / c1;
+    block_quotients(w, a0, q);
+    block_quotients(w + 8, a1, q + 8);
+    // p[k]: the codes of the 4 weights of load k in the bytes of one word
+    uint32_t p[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) q[i] = div_by_block_absmax(w[i], c1, y);
-    } else {
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = (c1 > 0.0f) ? w[i] / c1 : 0.0f;
-        q[i] = v == 0.0f ? -0.0f : v;
-      }
-    }
-    // pack: per 8 weights, byte j = code(w_j) | code(w_{j+4}) << 4
-    uint32_t lo = 0, hi = 0;
+      for (int j = 0; j < 4; ++j) p[k] |= nf4_code(q[4 * k + j], s_lut) << (8 * j);
+    const uint32_t nib = (uint32_t)(t & 1) * 4u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= (nf4_code(q[j], s_lut) | (nf4_code(q[j + 4], s_lut) << 4)) << (8 * j);
-      hi |= (nf4_code(q[8 + j], s_lut) | (nf4_code(q[12 + j], s_lut) << 4)) << (8 * j);
-    }
-    if (valid) {
-      u32x2 pk = {lo, hi};
-      *reinterpret_cast<u32x2*>(codes + (blk0 + lb) * (kBlock / 2) + quarter * 8) = pk;
-    }
+    for (int k = 0; k < 4; ++k) p[k] = or_lane_pair(p[k] << nib);
+    // p[0], p[1]: words t/2 and 4 + t/2 of block lb; p[2], p[3]: of lb + 1
+    const bool odd = (t & 1) != 0;
+    const uint32_t off = (uint32_t)(lb + (odd ? 1 : 0)) * (kBlock / 2) + (uint32_t)(t >> 1) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b32(odd ? p[2] : p[0], cr, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(odd ? p[3] : p[1], cr, (int)(off + 16u), 0, 0);
   }
   __syncthreads();
 
