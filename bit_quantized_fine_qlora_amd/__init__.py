@@ -30,6 +30,7 @@ from .api import (  # noqa: F401
     profile_enable,
     profile_query,
     quantize_dq,
+    quantize_dq_grouped,
     quantize_nf4_dq,
     workspace_bytes,
 )

@@ -27,6 +27,11 @@ class LinearLayer(ctypes.Structure):
                 ("A", c_vp), ("B", c_vp), ("h", c_vp), ("u_out", c_vp)]
 
 
+class QuantWeight(ctypes.Structure):
+    """qlora_quant_weight: one weight of a grouped quantization (host struct)."""
+    _fields_ = [("W", c_vp), ("m", c_i64), ("n", c_i64), ("codes", c_vp), ("absmax8", c_vp), ("c2", c_vp)]
+
+
 class Dropout(ctypes.Structure):
     """qlora_dropout: dropout on the adapter input (host struct)."""
     _fields_ = [("p", c_f32), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64)]
@@ -47,6 +52,7 @@ PROTOTYPES = {
     "qlora_dequant_nf4_dq": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlora_level_table": (ctypes.c_int, [c_i32, c_vp, c_vp]),
     "qlora_quantize_dq": (ctypes.c_int, [c_i32, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "qlora_quantize_dq_grouped": (ctypes.c_int, [c_i32, c_i32, ctypes.POINTER(QuantWeight), c_vp]),
     "qlora_dequant_dq": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qlora_adam_step": (ctypes.c_int, [ctypes.POINTER(AdamTensor), c_i32, c_f32, c_f32, c_f32, c_f32, c_f32, c_i64,
                                        c_vp]),

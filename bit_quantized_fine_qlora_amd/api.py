@@ -78,6 +78,31 @@ def quantize_dq(W: torch.Tensor, qtype: int = QTYPE_NF4, out: QuantizedWeight | 
     return q
 
 
+def quantize_dq_grouped(Ws, qtype: int = QTYPE_NF4, outs=None):
+    """Quantize several fp32 weights in one launch, each as quantize_dq would.
+
+    Ws: sequence of up to 8 m x n fp32 tensors on one device; outs: matching
+    QuantizedWeights to write, or None to allocate.  Returns the list of
+    QuantizedWeights.
+    """
+    if not Ws:
+        return []
+    dev = Ws[0].device
+    arr = (_lib.QuantWeight * len(Ws))()
+    qs = []
+    for i, W in enumerate(Ws):
+        m, n = W.shape
+        _need(W, torch.float32, (m, n), "W")
+        if W.device != dev:
+            raise ValueError("quantize_dq_grouped: all weights must be on one device")
+        q = outs[i] if outs is not None else alloc_quantized(m, n, dev)
+        arr[i] = _lib.QuantWeight(_ptr(W), m, n, _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2))
+        qs.append(q)
+    st = _lib.load().qlora_quantize_dq_grouped(int(qtype), len(Ws), arr, _stream(dev))
+    _lib.check(st, "qlora_quantize_dq_grouped")
+    return qs
+
+
 def dequant_dq(q: QuantizedWeight, qtype: int = QTYPE_NF4) -> torch.Tensor:
     out = torch.empty((q.m, q.n), dtype=torch.bfloat16, device=q.codes.device)
     st = _lib.load().qlora_dequant_dq(int(qtype), _ptr(q.codes), _ptr(q.absmax8), _ptr(q.c2), q.m, q.n, _ptr(out),

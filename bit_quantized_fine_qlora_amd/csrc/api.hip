@@ -24,6 +24,16 @@ namespace qlora {
 // kernels (defined in the other translation units)
 void launch_quantize(const float* W, int64_t numel, uint8_t* codes, uint8_t* absmax8, float* c2,
                      const Nf4Table& tab, hipStream_t stream);
+struct QuantWeight {
+  const float* W;
+  int64_t numel;
+  uint8_t* codes;
+  uint8_t* absmax8;
+  float* c2;
+};
+int max_quant_weights();
+int64_t quant_groups(int64_t numel);
+void launch_quantize_grouped(const QuantWeight* w, int count, const Nf4Table& tab, hipStream_t stream);
 void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t numel, uint16_t* out,
                     const Nf4Table& tab, hipStream_t stream);
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
@@ -416,6 +426,29 @@ qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t
   {
     Timed tm("quantize", s);
     launch_quantize(W, m * n, codes, absmax8, c2, table(qtype), s);
+  }
+  return hip_status();
+}
+
+qlora_status qlora_quantize_dq_grouped(int32_t qtype, int32_t count, const qlora_quant_weight* weights,
+                                       qlora_stream_t stream) {
+  if (!valid_qtype(qtype)) return QLORA_ERR_VALUE;
+  if (!weights) return QLORA_ERR_NULL;
+  if (count < 1 || count > max_quant_weights()) return QLORA_ERR_VALUE;
+  QuantWeight w[8];
+  for (int i = 0; i < count; ++i) {
+    const qlora_quant_weight& q = weights[i];
+    if (!q.W || !q.codes || !q.absmax8 || !q.c2) return QLORA_ERR_NULL;
+    const qlora_status st = check_weight_shape(q.m, q.n);
+    if (st != QLORA_OK) return st;
+    if (!aligned16(q.W) || !aligned16(q.codes) || !aligned16(q.absmax8) || !aligned16(q.c2)) return QLORA_ERR_ALIGN;
+    w[i] = QuantWeight{q.W, q.m * q.n, q.codes, q.absmax8, q.c2};
+  }
+  // m n <= 2^40 per weight: at most 8 * 2^26 groups, one workgroup each
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm("quantize", s);
+    launch_quantize_grouped(w, count, table(qtype), s);
   }
   return hip_status();
 }

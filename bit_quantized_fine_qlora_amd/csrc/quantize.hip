@@ -107,17 +107,38 @@ constexpr int kAuxNonTemporal = 2;  // buffer access cache policy: nt
 // lane the other (weights 8p .. 8p + 3 low, 8p + 4 .. 8p + 7 high), merged
 // by one DPP exchange; even lanes store the first block's words, odd lanes
 // the second's.
-__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __restrict__ W, int64_t nblk,
-                                                               uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ absmax8,
-                                                               float* __restrict__ c2out, Nf4Table tab) {
+//
+// One launch serves up to kMaxQuantWeights weights: workgroup b takes group
+// b - grp_end[i - 1] of the weight i with grp_end[i - 1] <= b < grp_end[i]
+// (grp_end[-1] = 0), so weights too small to fill the chip alone share it.
+constexpr int kMaxQuantWeights = 8;
+struct QuantArgs {
+  const float* W[kMaxQuantWeights];
+  uint8_t* codes[kMaxQuantWeights];
+  uint8_t* absmax8[kMaxQuantWeights];
+  float* c2[kMaxQuantWeights];
+  int64_t nblk[kMaxQuantWeights];
+  int32_t grp_end[kMaxQuantWeights];  // groups of weights 0 .. i together
+  int32_t count;
+};
+
+__global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(QuantArgs qa, Nf4Table tab) {
   // code table (both halves) with the block constants and the group
   // maximum in the gap between the halves
   __shared__ uint2 s_lut[kCodeLutNegBase + kCodeLutSize];
   float* s_c1 = reinterpret_cast<float*>(s_lut + kCodeLutSize);
   float* s_red = s_c1 + kGroupBlocks;
   const int tid = threadIdx.x;
-  const int64_t blk0 = (int64_t)blockIdx.x * kGroupBlocks;
+  const int bid = (int)blockIdx.x;
+  int wi = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < kMaxQuantWeights; ++i) wi += (i + 1 < qa.count && bid >= qa.grp_end[i]) ? 1 : 0;
+  const float* __restrict__ W = qa.W[wi];
+  uint8_t* __restrict__ codes = qa.codes[wi];
+  uint8_t* __restrict__ absmax8 = qa.absmax8[wi];
+  const int64_t nblk = qa.nblk[wi];
+  const int grp = bid - (wi ? qa.grp_end[wi - 1] : 0);
+  const int64_t blk0 = (int64_t)grp * kGroupBlocks;
   const int nb = (int)((nblk - blk0) < kGroupBlocks ? (nblk - blk0) : kGroupBlocks);
   const int lane = tid & 63, wave = tid >> 6;
   const int oct = lane >> 3, t = lane & 7;
@@ -203,7 +224,7 @@ __global__ __launch_bounds__(256) void quantize_nf4_dq_kernel(const float* __res
     const uint32_t code = c2 > 0.0f ? e4m3_encode_unit(c1 / c2) : 0u;
     absmax8[blk0 + tid] = (uint8_t)code;
   }
-  if (tid == 0) c2out[blockIdx.x] = c2;
+  if (tid == 0) qa.c2[wi][grp] = c2;
 }
 
 // W' = bf16(fl32(Q[code] * s_b)) for 8 consecutive weights per thread.
@@ -220,12 +241,41 @@ __global__ __launch_bounds__(256) void dequant_nf4_dq_kernel(const uint32_t* __r
   out[i] = u32x4{o[0], o[1], o[2], o[3]};
 }
 
+// Weights 0 .. count - 1 (count 1 .. kMaxQuantWeights), each of numel
+// elements (a multiple of 64), in one launch.
+struct QuantWeight {
+  const float* W;
+  int64_t numel;
+  uint8_t* codes;
+  uint8_t* absmax8;
+  float* c2;
+};
+
+int max_quant_weights() { return kMaxQuantWeights; }
+
+// Groups of a weight of numel elements.
+int64_t quant_groups(int64_t numel) { return (numel / kBlock + kGroupBlocks - 1) / kGroupBlocks; }
+
+void launch_quantize_grouped(const QuantWeight* w, int count, const Nf4Table& tab, hipStream_t stream) {
+  QuantArgs qa{};
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    qa.W[i] = w[i].W;
+    qa.codes[i] = w[i].codes;
+    qa.absmax8[i] = w[i].absmax8;
+    qa.c2[i] = w[i].c2;
+    qa.nblk[i] = w[i].numel / kBlock;
+    total += quant_groups(w[i].numel);
+    qa.grp_end[i] = (int32_t)total;
+  }
+  qa.count = count;
+  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)total), dim3(256), 0, stream, qa, tab);
+}
+
 void launch_quantize(const float* W, int64_t numel, uint8_t* codes, uint8_t* absmax8, float* c2,
                      const Nf4Table& tab, hipStream_t stream) {
-  const int64_t nblk = numel / kBlock;
-  const int64_t ngrp = (nblk + kGroupBlocks - 1) / kGroupBlocks;
-  hipLaunchKernelGGL(quantize_nf4_dq_kernel, dim3((unsigned)ngrp), dim3(256), 0, stream, W, nblk, codes, absmax8,
-                     c2, tab);
+  const QuantWeight w{W, numel, codes, absmax8, c2};
+  launch_quantize_grouped(&w, 1, tab, stream);
 }
 
 void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c2, int64_t numel, uint16_t* out,

@@ -202,6 +202,33 @@ qlora_status qlora_quantize_dq(int32_t qtype, const float* W, int64_t m, int64_t
 qlora_status qlora_dequant_dq(int32_t qtype, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                               int64_t m, int64_t n, qlora_bf16* W_out, qlora_stream_t stream);
 
+/*
+ * One weight of a grouped quantization (host struct): W, its shape and its
+ * outputs, each as for qlora_quantize_nf4_dq.
+ */
+typedef struct {
+  const float* W;
+  int64_t m, n;
+  uint8_t* codes;
+  uint8_t* absmax8;
+  float* c2;
+} qlora_quant_weight;
+
+/*
+ * Quantize `count` weights (for example the seven frozen weights of a
+ * transformer block) in one launch, each exactly as qlora_quantize_dq with
+ * the same qtype would (the same bits); one launch over all of them keeps the
+ * GPU's memory pipeline full where a weight alone has too few 16384-element
+ * groups to (1024 x 4096: 256 groups, one per compute unit).  The blocks of
+ * 64 and groups of 256 blocks are those of "QLoRA: Efficient Fine-Tuning",
+ * Steps 1 and 2.  `weights` is a host array read before the call returns;
+ * count 1..8; the weights' outputs must not overlap.  Errors as for
+ * qlora_quantize_dq (qtype, then the array: NULL, count), checked for every
+ * weight before anything is launched.
+ */
+qlora_status qlora_quantize_dq_grouped(int32_t qtype, int32_t count, const qlora_quant_weight* weights,
+                                       qlora_stream_t stream);
+
 /* Operation ids for qlora_workspace_bytes. */
 #define QLORA_OP_FWD 0
 #define QLORA_OP_BWD 1

@@ -92,6 +92,26 @@ def test_level_table_variant_argument_errors(lib):
     assert lib.qlora_dequant_dq(1, P, P, P, 4, 64, MIS, None) == -4
 
 
+def test_grouped_quantize_argument_errors(lib):
+    from bit_quantized_fine_qlora_amd import _lib
+    f = lib.qlora_quantize_dq_grouped
+
+    def arr(*ws):
+        a = (_lib.QuantWeight * max(len(ws), 1))()
+        for i, (W, m, n, codes) in enumerate(ws):
+            a[i] = _lib.QuantWeight(W, m, n, codes, P, P)
+        return a
+    good = (P, 4, 64, P)
+    assert f(4, 1, arr(good), None) == -7                  # unknown qtype first
+    assert f(0, 1, None, None) == -1
+    assert f(0, 0, arr(good), None) == -7                  # count 1..8
+    assert f(0, 9, arr(*[good] * 9), None) == -7
+    assert f(0, 2, arr(good, (None, 4, 64, P)), None) == -1
+    assert f(0, 2, arr(good, (P, 4, 60, P)), None) == -2   # every weight checked before launch
+    assert f(0, 2, arr(good, (P, 4, 64, MIS)), None) == -4
+    assert f(3, 2, arr(good, (P, 1 << 31, 64, P)), None) == -2
+
+
 def test_dequant_argument_errors(lib):
     f = lib.qlora_dequant_nf4_dq
     assert f(P, P, None, 4, 64, P, None) == -1

@@ -488,6 +488,65 @@ def test_int4_quantizer(Q, m, n):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------------------ grouped quantization
+
+GROUPED_SHAPES = [(256, 256), (203, 4160), (1, 64), (1000, 1024), (17, 960), (64, 256), (333, 192), (4, 4096)]
+
+
+@pytest.mark.parametrize("qtype", [0, 3])
+def test_grouped_quantizer_small(Q, qtype):
+    # eight weights in one launch (ragged last groups, a one-block weight, an
+    # all-zero block, an exact zero, a subnormal): bit-exact against the
+    # oracle and against one call per weight
+    table = None if qtype == 0 else O.int4_table()
+    Ws = []
+    for i, (m, n) in enumerate(GROUPED_SHAPES):
+        W = QI.custom_inputs(seed=700 + i, M=1, n=n, m=m, r=1)["W"]
+        if i == 1:
+            W[0, :64] = 0.0
+            W[2, 5] = 0.0
+            W[3, 7] = 1e-39
+        Ws.append(W)
+    dWs = [torch.from_numpy(W).cuda() for W in Ws]
+    say(f"grouped quantize qtype {qtype}: {len(Ws)} weights")
+    qs = Q.quantize_dq_grouped(dWs, qtype=qtype)
+    torch.cuda.synchronize()
+    for W, dW, q in zip(Ws, dWs, qs):
+        qw = O.quantize_nf4_dq(W, table=table)
+        check_quantizer(q, qw)
+        one = Q.quantize_dq(dW, qtype=qtype)
+        assert torch.equal(one.codes, q.codes) and torch.equal(one.absmax8, q.absmax8)
+        assert torch.equal(one.c2.view(torch.int32), q.c2.view(torch.int32))
+    # fewer weights into the same outputs: the same bits again
+    again = Q.quantize_dq_grouped(dWs[:3], qtype=qtype, outs=qs[:3])
+    torch.cuda.synchronize()
+    for W, q in zip(Ws[:3], again):
+        qw = O.quantize_nf4_dq(W, table=table)
+        check_quantizer(q, qw)
+
+
+def test_grouped_quantizer_8b_block(Q):
+    # the 8B-shaped block's seven weights in one launch = one call per weight,
+    # bit for bit (the single-weight path is checked against the oracle at
+    # these sizes elsewhere); the k weight also against the oracle directly
+    layers = QI.WORKLOADS[4]["layers"]
+    gen = torch.Generator(device="cuda").manual_seed(44)
+    dWs = [torch.randn((L.m, L.n), generator=gen, device="cuda").mul_(L.w_sigma) for L in layers]
+    say("grouped quantize 8B block (7 weights)")
+    qs = Q.quantize_dq_grouped(dWs)
+    torch.cuda.synchronize()
+    for L, dW, q in zip(layers, dWs, qs):
+        one = Q.quantize_nf4_dq(dW)
+        assert torch.equal(one.codes, q.codes), L.name
+        assert torch.equal(one.absmax8, q.absmax8), L.name
+        assert torch.equal(one.c2.view(torch.int32), q.c2.view(torch.int32)), L.name
+        del one
+    k = [i for i, L in enumerate(layers) if L.name == "k"][0]
+    check_quantizer(qs[k], O.quantize_nf4_dq(dWs[k].cpu().numpy()))
+    del qs, dWs
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ adapter merge
 
 def bf16_order(bits):
