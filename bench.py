@@ -68,25 +68,25 @@ BF16_PEAK_TFLOPS = 2500.0
 # kernel and the header it includes): reported as null once either changes.
 # The counters count the L2's requests to the memory fabric, so bytes served
 # by the last-level cache (MALL) are included: an upper bound on HBM bytes.
-# The k and v forwards are few-tile launches whose writes are the fp32 K
-# pieces, not h.
+# The k and v forwards run every tile as two K halves: their writes are h
+# plus one fp32 half-sum per tile.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "177549dbae367d2ff665f06957fc786270183bcf",
-    "q/fwd_gemm": {"fetch": 1297420843, "write": 134250837},
-    "k/fwd_gemm": {"fetch": 550731136, "write": 67108864},
-    "v/fwd_gemm": {"fetch": 550768597, "write": 67108864},
-    "o/fwd_gemm": {"fetch": 1296333525, "write": 134255531},
-    "gate/fwd_gemm": {"fetch": 4817727701, "write": 469857195},
-    "up/fwd_gemm": {"fetch": 4826893227, "write": 469820544},
-    "down/fwd_gemm": {"fetch": 4459527339, "write": 134222635},
-    "down/dgrad_gemm": {"fetch": 4604059349, "write": 469778347},
-    "up/dgrad_gemm": {"fetch": 4383778987, "write": 134225877},
-    "gate/dgrad_gemm": {"fetch": 4383752277, "write": 134227627},
-    "o/dgrad_gemm": {"fetch": 1278457813, "write": 134248832},
-    "v/dgrad_gemm": {"fetch": 191458091, "write": 134378880},
-    "k/dgrad_gemm": {"fetch": 191380181, "write": 134358997},
-    "q/dgrad_gemm": {"fetch": 1278411819, "write": 134246443},
+    "src_sha1": "f94115ce2d24b145f487c4b2102943d319854794",
+    "q/fwd_gemm": {"fetch": 1298033749, "write": 134250112},
+    "k/fwd_gemm": {"fetch": 584378794, "write": 50344533},
+    "v/fwd_gemm": {"fetch": 584300800, "write": 50344874},
+    "o/fwd_gemm": {"fetch": 1296274858, "write": 134253696},
+    "gate/fwd_gemm": {"fetch": 4823376554, "write": 469919978},
+    "up/fwd_gemm": {"fetch": 4820137941, "write": 469893930},
+    "down/fwd_gemm": {"fetch": 4458682880, "write": 134232320},
+    "down/dgrad_gemm": {"fetch": 4604084437, "write": 469835093},
+    "up/dgrad_gemm": {"fetch": 4383792512, "write": 134229632},
+    "gate/dgrad_gemm": {"fetch": 4383850197, "write": 134226773},
+    "o/dgrad_gemm": {"fetch": 1278500565, "write": 134244181},
+    "v/dgrad_gemm": {"fetch": 191530325, "write": 134373888},
+    "k/dgrad_gemm": {"fetch": 191357525, "write": 134409002},
+    "q/dgrad_gemm": {"fetch": 1278446037, "write": 134240725},
 }
 
 
