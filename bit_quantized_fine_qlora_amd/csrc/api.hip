@@ -201,17 +201,26 @@ struct Timed {
   Timed(const char* nm, hipStream_t st) : s(st), name(nm) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     on = g_prof_on && !t_prof_suppressed;
-    if (on) {
-      hipEventCreate(&a);
-      hipEventCreate(&b);
-      hipEventRecord(a, s);
+    // a launch whose events cannot be made or recorded is left untimed
+    if (on && (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess ||
+               hipEventRecord(a, s) != hipSuccess)) {
+      drop();
+      on = false;
     }
   }
   ~Timed() {
     if (!on) return;
-    hipEventRecord(b, s);
+    if (hipEventRecord(b, s) != hipSuccess) {
+      drop();
+      return;
+    }
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_recs.push_back(Rec{name, a, b});
+  }
+  void drop() {
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+    a = b = nullptr;
   }
 };
 
@@ -845,8 +854,8 @@ qlora_status qlora_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (on) {
     for (auto& rec : g_recs) {
-      hipEventDestroy(rec.a);
-      hipEventDestroy(rec.b);
+      (void)hipEventDestroy(rec.a);
+      (void)hipEventDestroy(rec.b);
     }
     g_recs.clear();
   }

@@ -336,6 +336,11 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   const int lq = lane >> 4;
   const int wf = (wave % (lg2::BF / WF)) * WF;
   const int wt = (wave / (lg2::BF / WF)) * WT;
+  // A wave whose tokens all lie past M (a ragged last token tile, few-token
+  // GEMMs) only reads zero rows: it skips its MFMAs and its piece store
+  // (the accumulators stay zero, and no output row past M is written), so
+  // for M <= 128 the remaining waves' MFMAs share the SIMDs.
+  const bool active = t0 + wt < p.M;
 
   f32x4 acc[NI][NJ];
 #pragma unroll
@@ -427,8 +432,10 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   const bool lora16 = !kBwd && p.r <= 16;  // a LoRA step then fills only its first K half
   auto step = [&](int ks, const uint8_t* w, const uint8_t* a, uint8_t* a_next) {
     if (ks + 1 < nk) copy_act(a_next);
-    mfma_step(w, a, 0);
-    if (!(lora16 && ks >= nk)) mfma_step(w, a, 1);
+    if (active) {
+      mfma_step(w, a, 0);
+      if (!(lora16 && ks >= nk)) mfma_step(w, a, 1);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
@@ -454,6 +461,8 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   if (kPieces) {
     // one K piece (few-tile mode): its fp32 sums, in the layout below, in
     // slot tile * pieces + piece (the work item's index) of piece_out
+    // (reduce_pieces_kernel reads no row past M)
+    if (!active) return;
     const brsrc_t r_pl = make_rsrc(p.piece_out + (size_t)blockIdx.x * (lg2::BF * lg2::BT), lg2::BF * lg2::BT * 4);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
