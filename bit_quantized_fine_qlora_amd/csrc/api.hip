@@ -87,7 +87,7 @@ struct AdamTensorHost {
 void launch_adam_step(const AdamTensorHost* ts, int count, float lr, float beta1, float beta2, float eps,
                       float weight_decay, int64_t step, hipStream_t stream);
 bool gpass_supported(int R);
-int gpass_splits_f(int64_t J, int R);
+int gpass_splits_f(int64_t M, int64_t J, int R);
 int gpass_splits_t(int64_t M);
 void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
                   float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream);
@@ -321,7 +321,7 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   w.v = L.take((size_t)M * r * sizeof(float));
   w.gA = L.take((size_t)w.sa * n * r * sizeof(float));
   w.gB = w.gpass ? 0 : L.take((size_t)w.sb * w.m_pad * r * sizeof(float));
-  w.vpart = w.gpass ? L.take((size_t)gpass_splits_f(w.m_pad, r) * M * r * sizeof(float)) : 0;
+  w.vpart = w.gpass ? L.take((size_t)gpass_splits_f(M, w.m_pad, r) * M * r * sizeof(float)) : 0;
   w.gbpart = w.gpass ? L.take((size_t)gpass_splits_t(M) * w.m_pad * r * sizeof(float)) : 0;
   // dropout: the masked adapter part of grad_x in fp32
   w.dterm = dropout ? L.take((size_t)M * n * sizeof(float)) : 0;
@@ -766,7 +766,7 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     Timed tm("gpass", hs);
     launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), nullptr,
                  grad_B, hs);
-    launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(mk, r), M, r, vplanes, v, nullptr, nullptr,
+    launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(M, mk, r), M, r, vplanes, v, nullptr, nullptr,
                          hs);
   } else {
     uint16_t* Bt = at<uint16_t>(workspace, w.Bt);

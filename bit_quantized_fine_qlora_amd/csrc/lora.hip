@@ -349,9 +349,12 @@ __global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restr
 // One read of g for both products that need it:
 //   vpart[fs][t][q]  = sum_{f in feature tile fs} g[t][f] * B[f][q]
 //   gbpart[ts][f][q] = sum_{t in token tile ts}  g[t][f] * u[t][q]
-// (v = sum_fs vpart, grad_B = s sum_ts gbpart).  A workgroup owns 256
-// tokens x 512 features of g and walks them as 16 sub-tiles of 64 x 128
-// (feature sub-tile outer).  Per sub-tile every wave adds 16 tokens' worth
+// (v = sum_fs vpart, grad_B = s sum_ts gbpart).  A workgroup owns 64 ST
+// tokens x 128 SF features of g (ST = SF = 1 up to 64 tokens, ST = 2 and
+// SF = 1 up to 128, otherwise ST = 4 and SF = 512 / (128 RB): few tokens
+// then still give one workgroup per 128 features instead of tiles that are
+// mostly past M) and walks them as ST SF sub-tiles of 64 x 128 (feature
+// sub-tile outer).  Per sub-tile every wave adds 16 tokens' worth
 // of v (A = g rows, B operand = B read transposed from its natural [f][q]
 // tile) and 32 features' worth of grad_B (A = g columns read transposed, B
 // operand = u as bf16 hi + lo planes [q][t]) into accumulators that live
@@ -360,11 +363,10 @@ __global__ __launch_bounds__(256) void token_grad_kernel(const uint16_t* __restr
 namespace gp {
 constexpr int TT = 64;        // tokens per sub-tile
 constexpr int FT = 128;       // features per sub-tile
-constexpr int ST = 4;         // sub-tiles along tokens per workgroup
 constexpr int GB = TT * 256;  // g sub-tile bytes
 }  // namespace gp
 
-template <int RB, int SF>
+template <int RB, int SF, int ST>
 __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__ G, int64_t M, int64_t J,
                                                     const uint16_t* __restrict__ Bm, int64_t m,
                                                     const float* __restrict__ U, int R, float* __restrict__ vpart,
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
   const int fs = (int)blockIdx.x % nfs;      // feature tile (v partial index)
   const int ts = (int)blockIdx.x / nfs;      // token tile (grad_B partial index)
   const int64_t f0 = (int64_t)fs * gp::FT * SF;
-  const int64_t t0 = (int64_t)ts * gp::TT * gp::ST;
+  const int64_t t0 = (int64_t)ts * gp::TT * ST;
 
   // Rank slots q >= R of the B tiles and u planes are never loaded: clear them.
   if (R < 16 * RB) {
@@ -421,8 +423,8 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
 
   // sub-tile i: feature sub-tile i / ST, token sub-tile i % ST
   auto load = [&](int i, u32x4(&gr)[4], u32x4(&br)[PPT], u32x4(&ur)[PPT]) {
-    const int64_t fb = f0 + (int64_t)(i / gp::ST) * gp::FT;
-    const int64_t tb = t0 + (int64_t)(i % gp::ST) * gp::TT;
+    const int64_t fb = f0 + (int64_t)(i / ST) * gp::FT;
+    const int64_t tb = t0 + (int64_t)(i % ST) * gp::TT;
     const bool fok = fb + 8 * pc < J;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -467,10 +469,10 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
     }
   };
 
-  f32x4 av[gp::ST][RB];        // v: tokens 64 ts' + 16 wave + 4 lk + e, rank 16 cb + lr
+  f32x4 av[ST][RB];        // v: tokens 64 ts' + 16 wave + 4 lk + e, rank 16 cb + lr
   f32x4 ab[SF][2][RB];     // grad_B: features 128 fs' + 32 wave + 16 ib + 4 lk + e, rank 16 cb + lr
 #pragma unroll
-  for (int i = 0; i < gp::ST; ++i)
+  for (int i = 0; i < ST; ++i)
 #pragma unroll
     for (int c = 0; c < RB; ++c) av[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
   const int tr_c = lr & 3;
   auto compute = [&](int buf, int i) {
     const uint8_t* base = lds + buf * STAGE;
-    const int fsub = i / gp::ST, tsub = i % gp::ST;
+    const int fsub = i / ST, tsub = i % ST;
     // v += g[16 wave + lr][f] B[f][q] over the 128 features
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
@@ -533,8 +535,8 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
   // D sub-tiles of loads in flight (register sets used round-robin), two LDS
   // buffers: sub-tile i is stored into buffer i % 2 once every wave has left
   // the compute of sub-tile i - 2 (the barrier of sub-tile i - 1)
-  constexpr int NS = gp::ST * SF;
-  constexpr int D = RB == 1 ? 4 : 2;
+  constexpr int NS = ST * SF;
+  constexpr int D = (RB == 1 ? 4 : 2) < NS ? (RB == 1 ? 4 : 2) : NS;
   u32x4 gr[D][4], br[D][PPT], ur[D][PPT];
 #pragma unroll
   for (int i = 0; i < D; ++i) load(i, gr[i], br[i], ur[i]);
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
 
   float* vdst = vpart + (int64_t)fs * M * R;
 #pragma unroll
-  for (int i = 0; i < gp::ST; ++i)
+  for (int i = 0; i < ST; ++i)
 #pragma unroll
     for (int cb = 0; cb < RB; ++cb) {
       const int q = 16 * cb + lr;
@@ -973,10 +975,11 @@ __global__ __launch_bounds__(256) void skinny_token_kernel(const uint16_t* __res
 // reduce_splits_kernel adds them) and, if Yout is given, also writes that
 // sum; grid y = 1 makes the planes P2 of a second factor Y2 (one part).  A
 // workgroup takes 8 tokens (8 R <= 1024 elements, up to 4 per thread) and
-// issues the loads of 4 splits of all its elements together, so a launch
-// waits for memory about ceil(nsplit / 4) times (with 64 tokens and one
+// issues the loads of 16 splits of all its elements together, so a launch
+// waits for memory about ceil(nsplit / 16) times (with 64 tokens and one
 // element's splits at a time it waited 16 times: 15.8 us for the 70B
-// block's v at r = 64, 8 splits).  The sums are staged in LDS, then thread
+// block's v at r = 64, 8 splits; the single-read g pass leaves one split
+// per 128 features for few tokens, 112 for the 8B gate projection).  The sums are staged in LDS, then thread
 // i < 2 R writes the 8 tokens of plane row i (16 bytes).
 constexpr int kPlaneTok = 8;
 __global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restrict__ Y, int nsplit, int64_t M, int R,
@@ -1002,15 +1005,16 @@ __global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restr
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < ns; k0 += 4) {
-    float v[4][E];
+  constexpr int KF = 16;  // splits whose loads go out together
+  for (int k0 = 0; k0 < ns; k0 += KF) {
+    float v[KF][E];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < KF; ++c)
 #pragma unroll
       for (int e = 0; e < E; ++e)
         v[c][e] = (k0 + c < ns && ok[e]) ? src[(int64_t)(k0 + c) * lim + base + threadIdx.x + 256 * e] : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < KF; ++c)
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (k0 + c < ns) acc[e] += v[c][e];
@@ -1230,20 +1234,30 @@ void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int6
 }
 
 // v and grad_B from one read of g (R % 8 == 0, R <= 32): vpart holds
-// gpass_splits_f(J, R) x M x R floats, gbpart gpass_splits_t(M) x J x R.
+// gpass_splits_f(M, J, R) x M x R floats, gbpart gpass_splits_t(M) x J x R.
 bool gpass_supported(int R) { return R % 8 == 0 && R <= 32; }
-static inline int gpass_sf(int R) { return R <= 16 ? 4 : 2; }
-int gpass_splits_f(int64_t J, int R) { return (int)cdiv(J, gp::FT * gpass_sf(R)); }
-int gpass_splits_t(int64_t M) { return (int)cdiv(M, gp::TT * gp::ST); }
+static inline int gpass_st(int64_t M) { return M <= 64 ? 1 : M <= 128 ? 2 : 4; }
+static inline int gpass_sf(int64_t M, int R) { return M <= 128 ? 1 : R <= 16 ? 4 : 2; }
+int gpass_splits_f(int64_t M, int64_t J, int R) { return (int)cdiv(J, gp::FT * gpass_sf(M, R)); }
+int gpass_splits_t(int64_t M) { return (int)cdiv(M, gp::TT * gpass_st(M)); }
 
 void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
                   float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream) {
-  const int sf = gpass_splits_f(J, R), st = gpass_splits_t(M);
+  const int sf = gpass_splits_f(M, J, R), st = gpass_splits_t(M);
   const dim3 grid((unsigned)((int64_t)sf * st));
-  if (R <= 16)
-    hipLaunchKernelGGL((gpass_kernel<1, 4>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
-  else
-    hipLaunchKernelGGL((gpass_kernel<2, 2>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart);
+  const int sub_t = gpass_st(M);
+#define QLORA_GPASS(RB_, SF_, ST_) \
+  hipLaunchKernelGGL((gpass_kernel<RB_, SF_, ST_>), grid, dim3(256), 0, stream, G, M, J, B, m, U, R, vpart, gbpart)
+  if (R <= 16) {
+    if (sub_t == 1) QLORA_GPASS(1, 1, 1);
+    else if (sub_t == 2) QLORA_GPASS(1, 1, 2);
+    else QLORA_GPASS(1, 4, 4);
+  } else {
+    if (sub_t == 1) QLORA_GPASS(2, 1, 1);
+    else if (sub_t == 2) QLORA_GPASS(2, 1, 2);
+    else QLORA_GPASS(2, 2, 4);
+  }
+#undef QLORA_GPASS
   if (v) {  // else the caller sums the v partials (factor_planes_kernel)
     const int64_t count = M * R;
     hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
