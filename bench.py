@@ -72,21 +72,21 @@ BF16_PEAK_TFLOPS = 2500.0
 # plus one fp32 half-sum per tile.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "f94115ce2d24b145f487c4b2102943d319854794",
-    "q/fwd_gemm": {"fetch": 1298033749, "write": 134250112},
-    "k/fwd_gemm": {"fetch": 584378794, "write": 50344533},
-    "v/fwd_gemm": {"fetch": 584300800, "write": 50344874},
-    "o/fwd_gemm": {"fetch": 1296274858, "write": 134253696},
-    "gate/fwd_gemm": {"fetch": 4823376554, "write": 469919978},
-    "up/fwd_gemm": {"fetch": 4820137941, "write": 469893930},
-    "down/fwd_gemm": {"fetch": 4458682880, "write": 134232320},
-    "down/dgrad_gemm": {"fetch": 4604084437, "write": 469835093},
-    "up/dgrad_gemm": {"fetch": 4383792512, "write": 134229632},
-    "gate/dgrad_gemm": {"fetch": 4383850197, "write": 134226773},
-    "o/dgrad_gemm": {"fetch": 1278500565, "write": 134244181},
-    "v/dgrad_gemm": {"fetch": 191530325, "write": 134373888},
-    "k/dgrad_gemm": {"fetch": 191357525, "write": 134409002},
-    "q/dgrad_gemm": {"fetch": 1278446037, "write": 134240725},
+    "src_sha1": "4256446685bb5ea5ff9da386c78ecf91d8a40b4e",
+    "q/fwd_gemm": {"fetch": 1298029909, "write": 134242026},
+    "k/fwd_gemm": {"fetch": 584388608, "write": 50344064},
+    "v/fwd_gemm": {"fetch": 584413994, "write": 50344405},
+    "o/fwd_gemm": {"fetch": 1297629141, "write": 134239445},
+    "gate/fwd_gemm": {"fetch": 4808267477, "write": 469883349},
+    "up/fwd_gemm": {"fetch": 4814827648, "write": 469872213},
+    "down/fwd_gemm": {"fetch": 4458023168, "write": 134229717},
+    "down/dgrad_gemm": {"fetch": 4604074581, "write": 469790720},
+    "up/dgrad_gemm": {"fetch": 4383803264, "write": 134224298},
+    "gate/dgrad_gemm": {"fetch": 4383751381, "write": 134223872},
+    "o/dgrad_gemm": {"fetch": 1278406869, "write": 134240768},
+    "v/dgrad_gemm": {"fetch": 191478570, "write": 134353920},
+    "k/dgrad_gemm": {"fetch": 191378474, "write": 134345770},
+    "q/dgrad_gemm": {"fetch": 1278356437, "write": 134241088},
 }
 
 

@@ -975,13 +975,15 @@ __global__ __launch_bounds__(256) void skinny_token_kernel(const uint16_t* __res
 // reduce_splits_kernel adds them) and, if Yout is given, also writes that
 // sum; grid y = 1 makes the planes P2 of a second factor Y2 (one part).  A
 // workgroup takes 8 tokens (8 R <= 1024 elements, up to 4 per thread) and
-// issues the loads of 16 splits of all its elements together, so a launch
-// waits for memory about ceil(nsplit / 16) times (with 64 tokens and one
+// issues the loads of 4 splits of all its elements together, so a launch
+// waits for memory about ceil(nsplit / 4) times (with 64 tokens and one
 // element's splits at a time it waited 16 times: 15.8 us for the 70B
-// block's v at r = 64, 8 splits; the single-read g pass leaves one split
-// per 128 features for few tokens, 112 for the 8B gate projection).  The sums are staged in LDS, then thread
+// block's v at r = 64, 8 splits).  Beyond 8 splits (the single-read g pass
+// leaves one per 128 features for few tokens, 112 for the 8B gate
+// projection) 16 go out together.  The sums are staged in LDS, then thread
 // i < 2 R writes the 8 tokens of plane row i (16 bytes).
 constexpr int kPlaneTok = 8;
+template <bool kMany>  // beyond 8 splits (a separate instantiation keeps the other's registers)
 __global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restrict__ Y, int nsplit, int64_t M, int R,
                                                             int64_t Mp, uint16_t* __restrict__ P,
                                                             float* __restrict__ Yout, const float* __restrict__ Y2,
@@ -1005,19 +1007,43 @@ __global__ __launch_bounds__(256) void factor_planes_kernel(const float* __restr
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  constexpr int KF = 16;  // splits whose loads go out together
-  for (int k0 = 0; k0 < ns; k0 += KF) {
-    float v[KF][E];
+  if (!kMany || ns <= 8) {
+    // 4 splits' loads at a time, each under its guard
+    for (int k0 = 0; k0 < ns; k0 += 4) {
+      float v[4][E];
 #pragma unroll
-    for (int c = 0; c < KF; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        v[c][e] = (k0 + c < ns && ok[e]) ? src[(int64_t)(k0 + c) * lim + base + threadIdx.x + 256 * e] : 0.0f;
+        for (int e = 0; e < E; ++e)
+          v[c][e] = (k0 + c < ns && ok[e]) ? src[(int64_t)(k0 + c) * lim + base + threadIdx.x + 256 * e] : 0.0f;
 #pragma unroll
-    for (int c = 0; c < KF; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (k0 + c < ns) acc[e] += v[c][e];
+        for (int e = 0; e < E; ++e)
+          if (k0 + c < ns) acc[e] += v[c][e];
+    }
+  } else {
+    // many splits (few tokens through the single-read g pass): 16 splits'
+    // loads go out together, unconditionally (a load under a branch makes
+    // the compiler wait for every load in flight where the paths meet):
+    // split indices past the end repeat the last one and element indices
+    // past the range read element 0; those values are added as +0, which
+    // leaves the sum's bits unchanged (it starts at +0 and so is never -0)
+    constexpr int KF = 16;
+    for (int k0 = 0; k0 < ns; k0 += KF) {
+      float v[KF][E];
+#pragma unroll
+      for (int c = 0; c < KF; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t k = k0 + c < ns ? k0 + c : ns - 1;
+          v[c][e] = src[k * lim + (ok[e] ? base + threadIdx.x + 256 * e : 0)];
+        }
+#pragma unroll
+      for (int c = 0; c < KF; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += (k0 + c < ns && ok[e]) ? v[c][e] : 0.0f;
+    }
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -1121,8 +1147,11 @@ size_t token_planes_bytes(int64_t M, int R) { return (size_t)2 * R * (size_t)(cd
 void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t* P, float* Yout, const float* Y2,
                           uint16_t* P2, hipStream_t stream) {
   const int64_t Mp = cdiv(M, 64) * 64;
-  hipLaunchKernelGGL(factor_planes_kernel, dim3((unsigned)(Mp / kPlaneTok), Y2 ? 2u : 1u), dim3(256), 0, stream, Y, nsplit,
-                     M, R, Mp, P, Yout, Y2, P2);
+  const dim3 grid((unsigned)(Mp / kPlaneTok), Y2 ? 2u : 1u);
+  if (nsplit > 8)
+    hipLaunchKernelGGL(factor_planes_kernel<true>, grid, dim3(256), 0, stream, Y, nsplit, M, R, Mp, P, Yout, Y2, P2);
+  else
+    hipLaunchKernelGGL(factor_planes_kernel<false>, grid, dim3(256), 0, stream, Y, nsplit, M, R, Mp, P, Yout, Y2, P2);
 }
 
 // out = bf16(s sum_t X[t][j] Y[t][q]) over the first Jout columns.  Unmasked
