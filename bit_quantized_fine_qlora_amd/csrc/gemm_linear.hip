@@ -323,7 +323,7 @@ __device__ __forceinline__ void gemm_producer(const GemmArgs& p, const Nf4Table&
 // 128 x 64 in the forward and 64 x 128 in the backward, where the W'
 // fragments come from half-rate transposed reads and the activation
 // fragments from full-rate ones (the 64 x 128 shape halves the former).
-template <bool kBwd, bool kPieces>
+template <bool kBwd, bool kPieces, bool kSkip>
 __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds& lds, int tid, int64_t f0,
                                               int64_t t0, int k0, int nk, bool lora, int split, uint32_t* lds_word) {
   constexpr int WF = kBwd ? 64 : 128;
@@ -339,8 +339,10 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
   // A wave whose tokens all lie past M (a ragged last token tile, few-token
   // GEMMs) only reads zero rows: it skips its MFMAs and its piece store
   // (the accumulators stay zero, and no output row past M is written), so
-  // for M <= 128 the remaining waves' MFMAs share the SIMDs.
-  const bool active = t0 + wt < p.M;
+  // for M <= 128 the remaining waves' MFMAs share the SIMDs.  Only launches
+  // with M % 256 != 0 test it (kSkip): the branch in the K loop costs the
+  // whole-tile GEMMs 2-3 %.
+  const bool active = !kSkip || t0 + wt < p.M;
 
   f32x4 acc[NI][NJ];
 #pragma unroll
@@ -588,7 +590,7 @@ __device__ __forceinline__ void gemm_consumer(const GemmArgs& p, const lg2::Lds&
 
 // kPieces: few-tile mode (every tile as p.pieces K pieces), a separate
 // instantiation so that the other kernels' register allocation is untouched.
-template <bool kBwd, bool kPieces>
+template <bool kBwd, bool kPieces, bool kSkip>
 __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, Nf4Table tab) {
   using T = lg2::Tile<kBwd>;
   __shared__ __align__(16) uint8_t sw0[T::W];
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(lg2::kThreads) void linear_gemm_kernel(GemmArgs p, 
   if (tid >= 64 * lg2::kMfmaWaves)
     gemm_producer<kBwd>(p, tab, lds, tid - 64 * lg2::kMfmaWaves, f0, t0, k0, ks, lora, split, &lds_word);
   else
-    gemm_consumer<kBwd, kPieces>(p, lds, tid, f0, t0, k0, ks, lora, split, &lds_word);
+    gemm_consumer<kBwd, kPieces, kSkip>(p, lds, tid, f0, t0, k0, ks, lora, split, &lds_word);
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
@@ -746,6 +748,23 @@ int64_t gemm_giveup_offset(int64_t M, int64_t N, int64_t K) {
   return ns * lg2::BF * lg2::BT * (int64_t)sizeof(float) + 2 * ns * (int64_t)sizeof(uint32_t);
 }
 
+template <bool kPieces>
+static void launch_gemm_kernel(bool bwd, bool skip, dim3 grid, const GemmArgs& p, const Nf4Table& tab,
+                               hipStream_t stream) {
+  const dim3 block(lg2::kThreads);
+  if (bwd) {
+    if (skip)
+      hipLaunchKernelGGL((linear_gemm_kernel<true, kPieces, true>), grid, block, 0, stream, p, tab);
+    else
+      hipLaunchKernelGGL((linear_gemm_kernel<true, kPieces, false>), grid, block, 0, stream, p, tab);
+  } else {
+    if (skip)
+      hipLaunchKernelGGL((linear_gemm_kernel<false, kPieces, true>), grid, block, 0, stream, p, tab);
+    else
+      hipLaunchKernelGGL((linear_gemm_kernel<false, kPieces, false>), grid, block, 0, stream, p, tab);
+  }
+}
+
 // split_ws: gemm_split_ws_bytes(M, N, K) bytes (16-byte aligned), or null to
 // run every tile whole.
 static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, const Nf4Table& tab,
@@ -762,10 +781,7 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
     p.nsplit = 0;
     p.partial = nullptr;
     p.split_sync = nullptr;
-    if (bwd)
-      hipLaunchKernelGGL((linear_gemm_kernel<true, true>), dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
-    else
-      hipLaunchKernelGGL((linear_gemm_kernel<false, true>), dim3(tiles * pc), dim3(lg2::kThreads), 0, stream, p, tab);
+    launch_gemm_kernel<true>(bwd, p.M % lg2::BT != 0, dim3(tiles * pc), p, tab, stream);
     const unsigned rblocks = (unsigned)tiles * (lg2::BF * lg2::BT / 4 / 256);
     if (bwd)
       hipLaunchKernelGGL(reduce_pieces_kernel<true>, dim3(rblocks), dim3(256), 0, stream, p);
@@ -786,10 +802,7 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
                        2 * ns + 1);
   }
   const int grid = tiles + ns;
-  if (bwd)
-    hipLaunchKernelGGL((linear_gemm_kernel<true, false>), dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
-  else
-    hipLaunchKernelGGL((linear_gemm_kernel<false, false>), dim3(grid), dim3(lg2::kThreads), 0, stream, p, tab);
+  launch_gemm_kernel<false>(bwd, p.M % lg2::BT != 0, dim3(grid), p, tab, stream);
 }
 
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
