@@ -72,21 +72,21 @@ BF16_PEAK_TFLOPS = 2500.0
 # plus one fp32 half-sum per tile.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "4256446685bb5ea5ff9da386c78ecf91d8a40b4e",
-    "q/fwd_gemm": {"fetch": 1298029909, "write": 134242026},
-    "k/fwd_gemm": {"fetch": 584388608, "write": 50344064},
-    "v/fwd_gemm": {"fetch": 584413994, "write": 50344405},
-    "o/fwd_gemm": {"fetch": 1297629141, "write": 134239445},
-    "gate/fwd_gemm": {"fetch": 4808267477, "write": 469883349},
-    "up/fwd_gemm": {"fetch": 4814827648, "write": 469872213},
-    "down/fwd_gemm": {"fetch": 4458023168, "write": 134229717},
-    "down/dgrad_gemm": {"fetch": 4604074581, "write": 469790720},
-    "up/dgrad_gemm": {"fetch": 4383803264, "write": 134224298},
-    "gate/dgrad_gemm": {"fetch": 4383751381, "write": 134223872},
-    "o/dgrad_gemm": {"fetch": 1278406869, "write": 134240768},
-    "v/dgrad_gemm": {"fetch": 191478570, "write": 134353920},
-    "k/dgrad_gemm": {"fetch": 191378474, "write": 134345770},
-    "q/dgrad_gemm": {"fetch": 1278356437, "write": 134241088},
+    "src_sha1": "bf45b0a7d811dfb2fb5f3655e9edcfa8b639afad",
+    "q/fwd_gemm": {"fetch": 1297776341, "write": 134244181},
+    "k/fwd_gemm": {"fetch": 584369237, "write": 50344192},
+    "v/fwd_gemm": {"fetch": 584357674, "write": 50344448},
+    "o/fwd_gemm": {"fetch": 1296405034, "write": 134237866},
+    "gate/fwd_gemm": {"fetch": 4820334720, "write": 469909632},
+    "up/fwd_gemm": {"fetch": 4837583104, "write": 469846400},
+    "down/fwd_gemm": {"fetch": 4462549077, "write": 134228650},
+    "down/dgrad_gemm": {"fetch": 4603944533, "write": 469784661},
+    "up/dgrad_gemm": {"fetch": 4383796736, "write": 134230272},
+    "gate/dgrad_gemm": {"fetch": 4383850069, "write": 134225365},
+    "o/dgrad_gemm": {"fetch": 1278521301, "write": 134245248},
+    "v/dgrad_gemm": {"fetch": 191524309, "write": 134411264},
+    "k/dgrad_gemm": {"fetch": 191381674, "write": 134348842},
+    "q/dgrad_gemm": {"fetch": 1278447786, "write": 134242773},
 }
 
 
