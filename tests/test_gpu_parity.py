@@ -102,6 +102,12 @@ RAGGED = [
     (257, 448, 259, 7, 3.0),
     (200, 256, 1000, 32, 1.0),
     (77, 128, 333, 8, 2.0),
+    # the single-read g pass sized by M (r % 8 = 0, r <= 32): one 64-token
+    # sub-tile per workgroup with more than 8 v partials (the 16-wide planes
+    # sum), two sub-tiles at 32 ranks (likewise), one at 24 ranks
+    (64, 256, 2100, 16, 2.0),
+    (100, 320, 1500, 32, 1.5),
+    (40, 256, 300, 24, 0.5),
 ]
 
 
