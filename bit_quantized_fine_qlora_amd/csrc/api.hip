@@ -69,6 +69,9 @@ void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t
                           uint16_t* P2, hipStream_t stream);
 void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int64_t n, int R, float scale,
                               const DropoutDev& drop, float* out, hipStream_t stream);
+bool down_proj_bt_supported(int R);
+void launch_down_proj_bt(const uint16_t* G, int64_t M, int64_t K, const uint16_t* B, int64_t m, int R, float* part,
+                         int splits, hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
@@ -314,7 +317,8 @@ BwdWs bwd_ws(int64_t M, int64_t n, int64_t m, int32_t r, bool dropout = false) {
   w.sa = token_grad_splits(M, n, r);
   w.sb = token_grad_splits(M, w.m_pad, r);
   w.gpass = gpass_supported(r);
-  w.Bt = w.gpass ? 0 : L.take((size_t)w.m_pad * r * 2);
+  // B^T for v = g B, except where the stream reads B itself
+  w.Bt = (w.gpass || down_proj_bt_supported(r)) ? 0 : L.take((size_t)w.m_pad * r * 2);
   const int suv = w.gpass ? w.su : (w.su > w.sv ? w.su : w.sv);
   w.part_uv = L.take((size_t)suv * M * r * sizeof(float));
   w.u = L.take((size_t)M * r * sizeof(float));
@@ -769,16 +773,20 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(M, mk, r), M, r, vplanes, v, nullptr, nullptr,
                          hs);
   } else {
-    uint16_t* Bt = at<uint16_t>(workspace, w.Bt);
     uint16_t* uplanes = at<uint16_t>(workspace, w.uplanes);
-    {
+    const bool bt = down_proj_bt_supported(r);
+    if (!bt) {
       Timed tm("transpose", hs);
-      launch_transpose_bf16(B, m, r, mk, Bt, hs);
+      launch_transpose_bf16(B, m, r, mk, at<uint16_t>(workspace, w.Bt), hs);
     }
     {
-      // v partials; then v, its planes and u's planes in one launch
+      // v partials (from B itself, or from its transposed copy); then v, its
+      // planes and u's planes in one launch
       Timed tm("down_proj", hs);
-      launch_down_proj(gk, M, mk, Bt, r, part, w.sv, nullptr, hs, nullptr, 1.0f);
+      if (bt)
+        launch_down_proj_bt(gk, M, mk, B, m, r, part, w.sv, hs);
+      else
+        launch_down_proj(gk, M, mk, at<uint16_t>(workspace, w.Bt), r, part, w.sv, nullptr, hs, nullptr, 1.0f);
       launch_factor_planes(part, w.sv, M, r, vplanes, v, uu, uplanes, hs);
     }
     {

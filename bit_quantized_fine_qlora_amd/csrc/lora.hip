@@ -755,11 +755,16 @@ __device__ __forceinline__ uint32_t swch(int row, int c) {
   return (uint32_t)(row * (16 * CH) + ((c ^ (row & (CH - 1))) << 4));
 }
 
-template <int RB, int NS, int CH>
+// kYT: Y is given as [k][q] (B itself, R = 16 RB ranks, rows past yrows
+// read as zero) instead of [q][k]; its stage tile keeps that layout (KS rows
+// of 32 RB bytes, loaded as contiguous 1 KB blocks) and the MFMA operand is
+// read transposed with ds_read_b64_tr_b16, so v = g B needs no copy of B^T.
+template <int RB, int NS, int CH, bool kYT>
 __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                           const uint16_t* __restrict__ Y, int R,
-                                                          float* __restrict__ part, int64_t kc) {
+                                                          float* __restrict__ part, int64_t kc, int64_t yrows) {
   static_assert(CH == 8 || CH == 16, "row chunks per stage");
+  static_assert(!kYT || CH == 8, "transposed rank operand: 64 k per stage");
   constexpr int KS = 8 * CH;               // k per stage
   constexpr int RPB = 64 / CH;             // rows per 1 KB load block
   constexpr int XPW = 32 / RPB;            // X blocks per wave (its 32 token rows)
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __rest
   const int64_t kend = (kbeg + kc < K) ? kbeg + kc : K;
   const int nst = (int)cdiv(kend - kbeg, KS);
   const uint32_t xbytes = (uint32_t)(M * K * 2);
-  const uint32_t ybytes = (uint32_t)((int64_t)R * K * 2);
+  const uint32_t ybytes = (uint32_t)((int64_t)R * (kYT ? yrows : K) * 2);
   const brsrc_t rx = make_rsrc(X, xbytes);
   const brsrc_t ry = make_rsrc(Y, ybytes);
   // A 1 KB load block holds RPB rows: lane l lands in row l / CH of the
@@ -810,9 +815,17 @@ __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < YPW; ++j) {
       const int blk = wave + 4 * j;
-      const int q = RPB * blk + drow;
-      const int64_t k = kb + 8 * (dslot ^ (q & (CH - 1)));
-      dma16(ry, stg + XB + blk * 1024, (k < kend && q < R) ? (uint32_t)(((int64_t)q * K + k) * 2) : ybytes);
+      if constexpr (kYT) {
+        // rows kb + 1024 / (32 RB) blk .. of B, 2 RB lanes a row (KS rows in all)
+        const int row = (1024 / (32 * RB)) * blk + lane / (2 * RB);
+        const int64_t k = kb + row;
+        const int c = lane % (2 * RB);
+        dma16(ry, stg + XB + blk * 1024, (k < kend && row < KS) ? (uint32_t)((k * R + 8 * c) * 2) : ybytes);
+      } else {
+        const int q = RPB * blk + drow;
+        const int64_t k = kb + 8 * (dslot ^ (q & (CH - 1)));
+        dma16(ry, stg + XB + blk * 1024, (k < kend && q < R) ? (uint32_t)(((int64_t)q * K + k) * 2) : ybytes);
+      }
     }
   };
   f32x4 acc[2][RB];
@@ -825,8 +838,19 @@ __global__ __launch_bounds__(256) void skinny_down_kernel(const uint16_t* __rest
     for (int kk = 0; kk < CH / 4; ++kk) {
       u32x4 bq[RB];
 #pragma unroll
-      for (int cb = 0; cb < RB; ++cb)
-        bq[cb] = *reinterpret_cast<const u32x4*>(stg + XB + swch<CH>(16 * cb + lr, 4 * kk + lq));
+      for (int cb = 0; cb < RB; ++cb) {
+        if constexpr (kYT) {
+          // k rows 32 kk + 8 lq + 4 h + lr / 4, ranks 16 cb + 4 (lr % 4) .. + 3
+          const uint8_t* src = stg + XB + (32 * kk + 8 * lq + (lr >> 2)) * (32 * RB) + 2 * (16 * cb + 4 * (lr & 3));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 4 * (32 * RB)));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+          bq[cb] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        } else {
+          bq[cb] = *reinterpret_cast<const u32x4*>(stg + XB + swch<CH>(16 * cb + lr, 4 * kk + lq));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(stg + swch<CH>(32 * wave + 16 * i + lr, 4 * kk + lq));
@@ -1114,16 +1138,31 @@ void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y
     const dim3 grid((unsigned)cdiv(M, sk::DT), (unsigned)splits);
     constexpr int CH = sk::DCH;
     switch (rank_blocks(R)) {
-      case 1: hipLaunchKernelGGL((skinny_down_kernel<1, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      case 2: hipLaunchKernelGGL((skinny_down_kernel<2, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      case 4: hipLaunchKernelGGL((skinny_down_kernel<4, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
-      default: hipLaunchKernelGGL((skinny_down_kernel<8, 3, CH>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc); break;
+      case 1: hipLaunchKernelGGL((skinny_down_kernel<1, 3, CH, false>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, K); break;
+      case 2: hipLaunchKernelGGL((skinny_down_kernel<2, 3, CH, false>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, K); break;
+      case 4: hipLaunchKernelGGL((skinny_down_kernel<4, 3, CH, false>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, K); break;
+      default: hipLaunchKernelGGL((skinny_down_kernel<8, 3, CH, false>), grid, dim3(256), 0, stream, X, M, K, Y, R, part, kc, K); break;
     }
   }
   if (!out) return;  // the caller sums the partials (factor_planes_kernel)
   const int64_t count = M * R;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
                      count, scale, out);
+}
+
+// v partials straight from B (m x R, R = 64 or 128): part[split][t][q] =
+// sum over the split's k of G[t][k] B[k][q], G M x K with K >= m (rows of B
+// past m read as zero).  The split rule and partial layout of
+// launch_down_proj.
+bool down_proj_bt_supported(int R) { return R == 64 || R == 128; }
+void launch_down_proj_bt(const uint16_t* G, int64_t M, int64_t K, const uint16_t* B, int64_t m, int R, float* part,
+                         int splits, hipStream_t stream) {
+  const int64_t kc = cdiv(cdiv(K, splits), dp::KCH) * dp::KCH;
+  const dim3 grid((unsigned)cdiv(M, sk::DT), (unsigned)splits);
+  if (R == 64)
+    hipLaunchKernelGGL((skinny_down_kernel<4, 3, 8, true>), grid, dim3(256), 0, stream, G, M, K, B, R, part, kc, m);
+  else
+    hipLaunchKernelGGL((skinny_down_kernel<8, 3, 8, true>), grid, dim3(256), 0, stream, G, M, K, B, R, part, kc, m);
 }
 
 // Token splits of a reduction over tokens: enough 128-column tiles x splits
