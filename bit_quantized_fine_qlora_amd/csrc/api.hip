@@ -72,6 +72,9 @@ void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int6
 bool down_proj_bt_supported(int R);
 void launch_down_proj_bt(const uint16_t* G, int64_t M, int64_t K, const uint16_t* B, int64_t m, int R, float* part,
                          int splits, hipStream_t stream);
+void launch_reduce_grads(const float* bpart, int nb_split, int64_t Jb, int64_t mb, float s_b, uint16_t* grad_B,
+                         const float* apart, int na_split, int64_t Ja, int64_t na, float s_a, uint16_t* grad_A, int R,
+                         hipStream_t stream);
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
@@ -769,7 +772,7 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     // its partials) with its bf16 planes for grad_A in one launch
     Timed tm("gpass", hs);
     launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), nullptr,
-                 grad_B, hs);
+                 nullptr, hs);
     launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(M, mk, r), M, r, vplanes, v, nullptr, nullptr,
                          hs);
   } else {
@@ -791,15 +794,22 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     }
     {
       Timed tm("token_grad", hs);
-      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, grad_B, hs, nullptr, uplanes,
+      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, nullptr, hs, nullptr, uplanes,
                         true);
     }
   }
   {
     Timed tm("token_grad", hs);
-    // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p)
-    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, grad_A, hs, &dd, vplanes,
+    // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p); then the split
+    // sums of grad_B and grad_A in one launch
+    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, nullptr, hs, &dd, vplanes,
                       true);
+    if (w.gpass)
+      launch_reduce_grads(at<float>(workspace, w.gbpart), gpass_splits_t(M), mk, m, s, grad_B,
+                          at<float>(workspace, w.gA), w.sa, n, n, s * inv_keep, grad_A, r, hs);
+    else
+      launch_reduce_grads(at<float>(workspace, w.gB), w.sb, mk, m, s, grad_B, at<float>(workspace, w.gA), w.sa, n, n,
+                          s * inv_keep, grad_A, r, hs);
   }
   if (grad_x) {
     if (drop) {

@@ -580,10 +580,9 @@ __global__ __launch_bounds__(256) void gpass_kernel(const uint16_t* __restrict__
 
 // out = bf16(s * sum_s part[s]) over the first Jout rows of part ([J][R] per
 // split); out is [Jout][R] or, when transpose_out, [R][Jout].
-__global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restrict__ part, int nsplit, int64_t J,
-                                                          int64_t Jout, int R, float s, int transpose_out,
-                                                          uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void reduce_grad_body(int64_t i, const float* __restrict__ part, int nsplit, int64_t J,
+                                                 int64_t Jout, int R, float s, int transpose_out,
+                                                 uint16_t* __restrict__ out) {
   if (i >= Jout * R) return;
   const float acc = sum_splits(part, nsplit, J * R, i);
   const uint16_t b = (uint16_t)(pack_bf16x2(s * acc, 0.f) & 0xFFFFu);
@@ -594,6 +593,11 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restric
     out[q * Jout + j] = b;
   }
 }
+__global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restrict__ part, int nsplit, int64_t J,
+                                                          int64_t Jout, int R, float s, int transpose_out,
+                                                          uint16_t* __restrict__ out) {
+  reduce_grad_body((int64_t)blockIdx.x * 256 + threadIdx.x, part, nsplit, J, Jout, R, s, transpose_out, out);
+}
 
 // The transposed case of reduce_grad_kernel (out [R][Jout]): thread (g, q)
 // sums rows j = 8 g .. 8 g + 7 at column q, each in split order from 0 as
@@ -601,10 +605,8 @@ __global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restric
 // out's row q.  A wave's loads of one row j are R consecutive floats, and
 // up to 16 loads of a thread are in flight together (one element per
 // thread wrote 2 bytes at stride Jout and waited for each element's loads).
-__global__ __launch_bounds__(256) void reduce_grad_t_kernel(const float* __restrict__ part, int nsplit, int64_t J,
-                                                            int64_t Jout, int R, float s,
-                                                            uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void reduce_grad_t_body(int64_t i, const float* __restrict__ part, int nsplit, int64_t J,
+                                                   int64_t Jout, int R, float s, uint16_t* __restrict__ out) {
   const int64_t groups = (Jout + 7) / 8;
   if (i >= groups * R) return;
   const int q = (int)(i % R);
@@ -634,6 +636,30 @@ __global__ __launch_bounds__(256) void reduce_grad_t_kernel(const float* __restr
     for (int e = 0; e < 8; ++e)
       if (j0 + e < Jout) dst[e] = (uint16_t)(pack_bf16x2(s * acc[e], 0.f) & 0xFFFFu);
   }
+}
+__global__ __launch_bounds__(256) void reduce_grad_t_kernel(const float* __restrict__ part, int nsplit, int64_t J,
+                                                            int64_t Jout, int R, float s,
+                                                            uint16_t* __restrict__ out) {
+  reduce_grad_t_body((int64_t)blockIdx.x * 256 + threadIdx.x, part, nsplit, J, Jout, R, s, out);
+}
+
+// Both adapter gradients' split sums in one launch: workgroups below nb
+// finish grad_B ([Jout][R], as reduce_grad_kernel), the rest grad_A ([R][Jout],
+// as reduce_grad_t_kernel); the same sums in the same order, so the same bits.
+struct GradSum {
+  const float* part;
+  int nsplit;
+  int64_t J, Jout;
+  int R;
+  float s;
+  uint16_t* out;
+};
+__global__ __launch_bounds__(256) void reduce_grads_kernel(GradSum b, GradSum a, int nb) {
+  if ((int)blockIdx.x < nb)
+    reduce_grad_body((int64_t)blockIdx.x * 256 + threadIdx.x, b.part, b.nsplit, b.J, b.Jout, b.R, b.s, 0, b.out);
+  else
+    reduce_grad_t_body((int64_t)(blockIdx.x - nb) * 256 + threadIdx.x, a.part, a.nsplit, a.J, a.Jout, a.R, a.s,
+                       a.out);
 }
 
 // out[r][0:cols] = in[r][0:cols], out[r][cols:cols_pad] = 0 (bf16 rows)
@@ -1220,6 +1246,7 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
       default: hipLaunchKernelGGL((skinny_token_kernel<8, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
     }
   }
+  if (!out) return;  // the caller sums the partials (launch_reduce_grads)
   const int64_t count = Jout * R;
   if (transpose_out)
     hipLaunchKernelGGL(reduce_grad_t_kernel, dim3((unsigned)cdiv(cdiv(Jout, 8) * R, 256)), dim3(256), 0, stream,
@@ -1227,6 +1254,20 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
   else
     hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
                        Jout, R, s, 0, out);
+}
+
+// grad_B = bf16(s_b sum of bpart's nb_split [Jb][R] partials) over the
+// first mb rows ([mb][R]) and grad_A = bf16(s_a sum of apart's na_split
+// [Ja][R] partials) over the first na rows, written transposed ([R][na]),
+// in one launch.
+void launch_reduce_grads(const float* bpart, int nb_split, int64_t Jb, int64_t mb, float s_b, uint16_t* grad_B,
+                         const float* apart, int na_split, int64_t Ja, int64_t na, float s_a, uint16_t* grad_A, int R,
+                         hipStream_t stream) {
+  const GradSum b{bpart, nb_split, Jb, mb, R, s_b, grad_B};
+  const GradSum a{apart, na_split, Ja, na, R, s_a, grad_A};
+  const int nbw = (int)cdiv(mb * R, 256);
+  const int naw = (int)cdiv(cdiv(na, 8) * R, 256);
+  hipLaunchKernelGGL(reduce_grads_kernel, dim3((unsigned)(nbw + naw)), dim3(256), 0, stream, b, a, nbw);
 }
 
 // The adapter part of grad_x under dropout, in fp32 for the grad_x GEMM to
@@ -1331,6 +1372,7 @@ void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, in
     hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
                        1.0f, v);
   }
+  if (!grad_B) return;  // the caller sums the grad_B partials (launch_reduce_grads)
   const int64_t gcount = m * R;
   hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(gcount, 256)), dim3(256), 0, stream, gbpart, st, J, m,
                      R, s, 0, grad_B);
