@@ -61,9 +61,8 @@ int down_proj_splits(int64_t M, int64_t K, int R);
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
                       float* out, hipStream_t stream, const DropoutDev* drop, float scale);
 int token_grad_splits(int64_t M, int64_t J, int R);
-void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
-                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop, uint16_t* planes, bool planes_ready);
+void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, int splits, float* part,
+                       hipStream_t stream, const DropoutDev* drop, uint16_t* planes, bool planes_ready);
 size_t token_planes_bytes(int64_t M, int R);
 void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t* P, float* Yout, const float* Y2,
                           uint16_t* P2, hipStream_t stream);
@@ -96,7 +95,7 @@ bool gpass_supported(int R);
 int gpass_splits_f(int64_t M, int64_t J, int R);
 int gpass_splits_t(int64_t M);
 void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
-                  float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream);
+                  float* vpart, float* gbpart, hipStream_t stream);
 
 namespace {
 
@@ -771,8 +770,7 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     // v = g B and grad_B = s g^T u from one read of g; then v (the sum of
     // its partials) with its bf16 planes for grad_A in one launch
     Timed tm("gpass", hs);
-    launch_gpass(gk, M, mk, B, m, uu, r, s, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), nullptr,
-                 nullptr, hs);
+    launch_gpass(gk, M, mk, B, m, uu, r, at<float>(workspace, w.vpart), at<float>(workspace, w.gbpart), hs);
     launch_factor_planes(at<float>(workspace, w.vpart), gpass_splits_f(M, mk, r), M, r, vplanes, v, nullptr, nullptr,
                          hs);
   } else {
@@ -794,16 +792,14 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
     }
     {
       Timed tm("token_grad", hs);
-      launch_token_grad(gk, M, mk, m, uu, r, s, w.sb, at<float>(workspace, w.gB), 0, nullptr, hs, nullptr, uplanes,
-                        true);
+      launch_token_grad(gk, M, mk, uu, r, w.sb, at<float>(workspace, w.gB), hs, nullptr, uplanes, true);
     }
   }
   {
     Timed tm("token_grad", hs);
     // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p); then the split
     // sums of grad_B and grad_A in one launch
-    launch_token_grad(x, M, n, n, v, r, s * inv_keep, w.sa, at<float>(workspace, w.gA), 1, nullptr, hs, &dd, vplanes,
-                      true);
+    launch_token_grad(x, M, n, v, r, w.sa, at<float>(workspace, w.gA), hs, &dd, vplanes, true);
     if (w.gpass)
       launch_reduce_grads(at<float>(workspace, w.gbpart), gpass_splits_t(M), mk, m, s, grad_B,
                           at<float>(workspace, w.gA), w.sa, n, n, s * inv_keep, grad_A, r, hs);

@@ -593,13 +593,8 @@ __device__ __forceinline__ void reduce_grad_body(int64_t i, const float* __restr
     out[q * Jout + j] = b;
   }
 }
-__global__ __launch_bounds__(256) void reduce_grad_kernel(const float* __restrict__ part, int nsplit, int64_t J,
-                                                          int64_t Jout, int R, float s, int transpose_out,
-                                                          uint16_t* __restrict__ out) {
-  reduce_grad_body((int64_t)blockIdx.x * 256 + threadIdx.x, part, nsplit, J, Jout, R, s, transpose_out, out);
-}
 
-// The transposed case of reduce_grad_kernel (out [R][Jout]): thread (g, q)
+// The transposed case of reduce_grad_body (out [R][Jout]): thread (g, q)
 // sums rows j = 8 g .. 8 g + 7 at column q, each in split order from 0 as
 // sum_splits adds them, and writes the 8 results as 16 contiguous bytes of
 // out's row q.  A wave's loads of one row j are R consecutive floats, and
@@ -637,15 +632,10 @@ __device__ __forceinline__ void reduce_grad_t_body(int64_t i, const float* __res
       if (j0 + e < Jout) dst[e] = (uint16_t)(pack_bf16x2(s * acc[e], 0.f) & 0xFFFFu);
   }
 }
-__global__ __launch_bounds__(256) void reduce_grad_t_kernel(const float* __restrict__ part, int nsplit, int64_t J,
-                                                            int64_t Jout, int R, float s,
-                                                            uint16_t* __restrict__ out) {
-  reduce_grad_t_body((int64_t)blockIdx.x * 256 + threadIdx.x, part, nsplit, J, Jout, R, s, out);
-}
 
 // Both adapter gradients' split sums in one launch: workgroups below nb
-// finish grad_B ([Jout][R], as reduce_grad_kernel), the rest grad_A ([R][Jout],
-// as reduce_grad_t_kernel); the same sums in the same order, so the same bits.
+// finish grad_B ([Jout][R], reduce_grad_body), the rest grad_A ([R][Jout],
+// reduce_grad_t_body); each sum adds the splits in order from 0.
 struct GradSum {
   const float* part;
   int nsplit;
@@ -1219,13 +1209,13 @@ void launch_factor_planes(const float* Y, int nsplit, int64_t M, int R, uint16_t
     hipLaunchKernelGGL(factor_planes_kernel<false>, grid, dim3(256), 0, stream, Y, nsplit, M, R, Mp, P, Yout, Y2, P2);
 }
 
-// out = bf16(s sum_t X[t][j] Y[t][q]) over the first Jout columns.  Unmasked
-// reductions stream through skinny_token_kernel from Y's bf16 hi / lo planes
-// (`planes`, token_planes_bytes), made here unless planes_ready; masked ones
-// (drop on) take token_grad_kernel, which reads Y itself.
-void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, const float* Y, int R, float s,
-                       int splits, float* part, int transpose_out, uint16_t* out, hipStream_t stream,
-                       const DropoutDev* drop, uint16_t* planes, bool planes_ready) {
+// part[split][j][q] = sum over the split's tokens of X[t][j] Y[t][q]; the
+// caller sums the splits (launch_reduce_grads).  Unmasked reductions stream
+// through skinny_token_kernel from Y's bf16 hi / lo planes (`planes`,
+// token_planes_bytes), made here unless planes_ready; masked ones (drop on)
+// take token_grad_kernel, which reads Y itself.
+void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, int splits, float* part,
+                       hipStream_t stream, const DropoutDev* drop, uint16_t* planes, bool planes_ready) {
   const int64_t tc = cdiv(cdiv(M, splits), tg::TT) * tg::TT;
   const dim3 grid((unsigned)cdiv(J, tg::JT), (unsigned)splits);
   if (drop && drop->on) {
@@ -1246,14 +1236,6 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, int64_t Jout, co
       default: hipLaunchKernelGGL((skinny_token_kernel<8, 3>), grid, dim3(256), 0, stream, X, M, J, planes, Mp, R, part, tc); break;
     }
   }
-  if (!out) return;  // the caller sums the partials (launch_reduce_grads)
-  const int64_t count = Jout * R;
-  if (transpose_out)
-    hipLaunchKernelGGL(reduce_grad_t_kernel, dim3((unsigned)cdiv(cdiv(Jout, 8) * R, 256)), dim3(256), 0, stream,
-                       part, splits, J, Jout, R, s, out);
-  else
-    hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits, J,
-                       Jout, R, s, 0, out);
 }
 
 // grad_B = bf16(s_b sum of bpart's nb_split [Jb][R] partials) over the
@@ -1342,8 +1324,10 @@ void launch_lora_dropout_term(const float* v, const uint16_t* A, int64_t M, int6
   }
 }
 
-// v and grad_B from one read of g (R % 8 == 0, R <= 32): vpart holds
-// gpass_splits_f(M, J, R) x M x R floats, gbpart gpass_splits_t(M) x J x R.
+// v and grad_B partials from one read of g (R % 8 == 0, R <= 32): vpart
+// holds gpass_splits_f(M, J, R) x M x R floats (summed by
+// factor_planes_kernel), gbpart gpass_splits_t(M) x J x R (summed by
+// launch_reduce_grads).
 bool gpass_supported(int R) { return R % 8 == 0 && R <= 32; }
 static inline int gpass_st(int64_t M) { return M <= 64 ? 1 : M <= 128 ? 2 : 4; }
 static inline int gpass_sf(int64_t M, int R) { return M <= 128 ? 1 : R <= 16 ? 4 : 2; }
@@ -1351,7 +1335,7 @@ int gpass_splits_f(int64_t M, int64_t J, int R) { return (int)cdiv(J, gp::FT * g
 int gpass_splits_t(int64_t M) { return (int)cdiv(M, gp::TT * gpass_st(M)); }
 
 void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, int64_t m, const float* U, int R,
-                  float s, float* vpart, float* gbpart, float* v, uint16_t* grad_B, hipStream_t stream) {
+                  float* vpart, float* gbpart, hipStream_t stream) {
   const int sf = gpass_splits_f(M, J, R), st = gpass_splits_t(M);
   const dim3 grid((unsigned)((int64_t)sf * st));
   const int sub_t = gpass_st(M);
@@ -1367,15 +1351,6 @@ void launch_gpass(const uint16_t* G, int64_t M, int64_t J, const uint16_t* B, in
     else QLORA_GPASS(2, 2, 4);
   }
 #undef QLORA_GPASS
-  if (v) {  // else the caller sums the v partials (factor_planes_kernel)
-    const int64_t count = M * R;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, vpart, sf, count,
-                       1.0f, v);
-  }
-  if (!grad_B) return;  // the caller sums the grad_B partials (launch_reduce_grads)
-  const int64_t gcount = m * R;
-  hipLaunchKernelGGL(reduce_grad_kernel, dim3((unsigned)cdiv(gcount, 256)), dim3(256), 0, stream, gbpart, st, J, m,
-                     R, s, 0, grad_B);
 }
 
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
