@@ -37,7 +37,7 @@ constexpr int PIECE = 256;   // k per piece (32 bytes of codes per lane)
 constexpr int kPW = (KC / 4) / PIECE;   // pieces per wave and feature block (2)
 constexpr int kDepth = 2;    // code pieces in flight per wave (deeper queues only delay x)
 constexpr int kMaxLayers = 8;
-constexpr int kTargetWGs = 512;         // two workgroups per CU
+constexpr int kWGsPerCU = 2;            // workgroups per CU a launch is sized for
 constexpr int XCPR = KC / 4 / 8;         // 16-byte chunks of one token row of a wave's x quarter
 constexpr int XRPL = 64 / XCPR;          // token rows per 64-lane load of the x quarter
 }  // namespace sm
@@ -652,8 +652,9 @@ void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4T
     for (int i = 0; i < count; ++i) w += small_nkc(layers[i].n) * (cdiv_s(cdiv_s(layers[i].m, 16), fbw) + 1);
     return w;
   };
+  const int64_t target = (int64_t)sm::kWGsPerCU * device_cus();
   int fbw = 1;
-  while (fbw < fbmax && wgs_for(fbw) > sm::kTargetWGs) ++fbw;
+  while (fbw < fbmax && wgs_for(fbw) > target) ++fbw;
   int wg = 0;
   int64_t outs = 0;
   for (int i = 0; i < count; ++i) {
