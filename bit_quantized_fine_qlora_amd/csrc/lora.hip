@@ -1120,16 +1120,32 @@ static inline int token_stages(int R) { return rank_blocks(R) == 4 ? 4 : 3; }
 static inline int down_wgs_per_cu(int R) { return rank_blocks(R) <= 4 ? 2 : 1; }
 static inline int token_wgs_per_cu(int R) { return rank_blocks(R) <= 2 ? 2 : 1; }
 
+// Split count s in 1 .. most for `tiles` tiles on `slots` resident
+// workgroups: the stream takes about ceil(tiles s / slots) rounds of 1 / s of
+// a tile's work, so the one with the fewest rounds per split wins (ties: the
+// larger s).  E.g. 112 column tiles on 256 slots: 2 splits (224 workgroups,
+// one round) instead of 3 (336 workgroups, a second round of 80).
+static int64_t fewest_rounds_splits(int64_t tiles, int64_t slots, int64_t most) {
+  int64_t best = 1;
+  for (int64_t sp = 1; sp <= most; ++sp) {
+    // rounds(sp) / sp <= rounds(best) / best, in integers
+    if (cdiv(tiles * sp, slots) * best <= cdiv(tiles * best, slots) * sp) best = sp;
+  }
+  return best;
+}
+
 // K splits of a down product: enough 128-token tiles x splits to fill every
 // CU with its resident workgroups, at most 64 splits, each at least 512 k
 // long and a multiple of 128 (the masked kernel takes 128-k stages).
 int down_proj_splits(int64_t M, int64_t K, int R) {
   const int64_t tiles = cdiv(M, sk::DT);
-  int64_t want = cdiv((int64_t)down_wgs_per_cu(R) * device_cus(), tiles);
+  const int64_t slots = (int64_t)down_wgs_per_cu(R) * device_cus();
+  int64_t want = cdiv(slots, tiles);
   const int64_t most = cdiv(K, 512);
   if (want > most) want = most;
   if (want > 64) want = 64;
   if (want < 1) want = 1;
+  want = fewest_rounds_splits(tiles, slots, want);
   return (int)cdiv(K, cdiv(cdiv(K, want), dp::KCH) * dp::KCH);
 }
 
@@ -1185,11 +1201,13 @@ void launch_down_proj_bt(const uint16_t* G, int64_t M, int64_t K, const uint16_t
 // to fill every CU, at most 64 splits of at least 512 tokens (multiples of 64).
 int token_grad_splits(int64_t M, int64_t J, int R) {
   const int64_t tiles = cdiv(J, tg::JT);
-  int64_t want = cdiv((int64_t)token_wgs_per_cu(R) * device_cus(), tiles);
+  const int64_t slots = (int64_t)token_wgs_per_cu(R) * device_cus();
+  int64_t want = cdiv(slots, tiles);
   const int64_t most = cdiv(M, 512);
   if (want > most) want = most;
   if (want > 64) want = 64;
   if (want < 1) want = 1;
+  want = fewest_rounds_splits(tiles, slots, want);
   return (int)cdiv(M, cdiv(cdiv(M, want), tg::TT) * tg::TT);
 }
 
