@@ -38,13 +38,14 @@ void launch_dequant(const uint8_t* codes, const uint8_t* absmax8, const float* c
                     const Nf4Table& tab, hipStream_t stream);
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
-                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream);
+                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream, bool sync_zeroed = false);
 size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K);
+SyncZero gemm_split_sync(int64_t M, int64_t N, int64_t K, void* split_ws);
 int64_t gemm_giveup_offset(int64_t M, int64_t N, int64_t K);
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream,
-                       const float* add);
+                       const float* add, bool sync_zeroed = false);
 int small_max_tokens();
 int small_max_layers();
 size_t small_ws_bytes(int64_t M, int64_t n, int64_t m, int r);
@@ -59,7 +60,8 @@ struct SmallLayerHost {
 void launch_small_fwd(int M, const SmallLayerHost* layers, int count, const Nf4Table& tab, hipStream_t stream);
 int down_proj_splits(int64_t M, int64_t K, int R);
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
-                      float* out, hipStream_t stream, const DropoutDev* drop, float scale);
+                      float* out, hipStream_t stream, const DropoutDev* drop, float scale,
+                      SyncZero z = SyncZero{});
 int token_grad_splits(int64_t M, int64_t J, int R);
 void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, int R, int splits, float* part,
                        hipStream_t stream, const DropoutDev* drop, uint16_t* planes, bool planes_ready);
@@ -73,7 +75,8 @@ void launch_down_proj_bt(const uint16_t* G, int64_t M, int64_t K, const uint16_t
                          int splits, hipStream_t stream);
 void launch_reduce_grads(const float* bpart, int nb_split, int64_t Jb, int64_t mb, float s_b, uint16_t* grad_B,
                          const float* apart, int na_split, int64_t Ja, int64_t na, float s_a, uint16_t* grad_A, int R,
-                         hipStream_t stream);
+                         hipStream_t stream,
+                         SyncZero z = SyncZero{});
 void launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld, uint16_t* out,
                            hipStream_t stream);
 void launch_pad_cols_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t cols_pad, uint16_t* out,
@@ -601,14 +604,16 @@ static qlora_status run_fwd(int64_t M, int64_t n, int64_t m, int32_t r, float s,
     return hip_status();
   }
   float* u = u_out ? u_out : at<float>(workspace, w.u);
+  void* ksplit = (use_ksplit && w.has_ksplit) ? at<uint8_t>(workspace, w.ksplit) : nullptr;
   {
+    // u's split sum also clears the GEMM's hand-off words
     Timed tm("down_proj", hs);
-    launch_down_proj(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs, &dd, inv_keep);
+    launch_down_proj(x, M, n, A, r, at<float>(workspace, w.part), w.splits, u, hs, &dd, inv_keep,
+                     gemm_split_sync(M, m, n, ksplit));
   }
   {
     Timed tm("fwd_gemm", hs);
-    launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s,
-                    (use_ksplit && w.has_ksplit) ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs);
+    launch_fwd_gemm(x, codes, absmax8, c2, B, u, h, M, n, m, r, s, ksplit, table(), hs, true);
   }
   return hip_status();
 }
@@ -795,17 +800,20 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
       launch_token_grad(gk, M, mk, uu, r, w.sb, at<float>(workspace, w.gB), hs, nullptr, uplanes, true);
     }
   }
+  void* ksplit = (grad_x && w.has_ksplit) ? at<uint8_t>(workspace, w.ksplit) : nullptr;
   {
     Timed tm("token_grad", hs);
     // grad_A = s v^T x_d with x_d = (x * keep) / (1 - p); then the split
-    // sums of grad_B and grad_A in one launch
+    // sums of grad_B and grad_A in one launch, which also clears the grad_x
+    // GEMM's hand-off words
     launch_token_grad(x, M, n, v, r, w.sa, at<float>(workspace, w.gA), hs, &dd, vplanes, true);
+    const SyncZero z = gemm_split_sync(M, n, w.m_pad, ksplit);
     if (w.gpass)
       launch_reduce_grads(at<float>(workspace, w.gbpart), gpass_splits_t(M), mk, m, s, grad_B,
-                          at<float>(workspace, w.gA), w.sa, n, n, s * inv_keep, grad_A, r, hs);
+                          at<float>(workspace, w.gA), w.sa, n, n, s * inv_keep, grad_A, r, hs, z);
     else
       launch_reduce_grads(at<float>(workspace, w.gB), w.sb, mk, m, s, grad_B, at<float>(workspace, w.gA), w.sa, n, n,
-                          s * inv_keep, grad_A, r, hs);
+                          s * inv_keep, grad_A, r, hs, z);
   }
   if (grad_x) {
     if (drop) {
@@ -817,12 +825,12 @@ qlora_status qlora_linear_bwd_ex(int64_t M, int64_t n, int64_t m, int32_t r, flo
         launch_lora_dropout_term(v, A, M, n, r, s * inv_keep, dd, dterm, hs);
       }
       Timed tm("dgrad_gemm", hs);
-      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, 0, s,
-                        w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs, dterm);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, 0, s, ksplit, table(), hs, dterm,
+                        true);
     } else {
       Timed tm("dgrad_gemm", hs);
-      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s,
-                        w.has_ksplit ? at<uint8_t>(workspace, w.ksplit) : nullptr, table(), hs, nullptr);
+      launch_dgrad_gemm(gk, codes, absmax8, c2, A, v, grad_x, M, n, m, w.m_pad, r, s, ksplit, table(), hs, nullptr,
+                        true);
     }
   }
   return hip_status();

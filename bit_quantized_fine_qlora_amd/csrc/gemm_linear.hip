@@ -748,6 +748,18 @@ int64_t gemm_giveup_offset(int64_t M, int64_t N, int64_t K) {
   return ns * lg2::BF * lg2::BT * (int64_t)sizeof(float) + 2 * ns * (int64_t)sizeof(uint32_t);
 }
 
+// The hand-off words of a GEMM on split_ws (none without a split or with K
+// pieces), for the kernel before it to clear.
+SyncZero gemm_split_sync(int64_t M, int64_t N, int64_t K, void* split_ws) {
+  SyncZero z;
+  if (!split_ws || gemm_pieces(M, N, K) > 1) return z;
+  const int64_t ns = gemm_split_tiles(M, N, K);
+  if (!ns) return z;
+  z.p = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(split_ws) + (size_t)ns * lg2::BF * lg2::BT * sizeof(float));
+  z.n = (int)(2 * ns + 1);
+  return z;
+}
+
 template <bool kPieces>
 static void launch_gemm_kernel(bool bwd, bool skip, dim3 grid, const GemmArgs& p, const Nf4Table& tab,
                                hipStream_t stream) {
@@ -766,9 +778,10 @@ static void launch_gemm_kernel(bool bwd, bool skip, dim3 grid, const GemmArgs& p
 }
 
 // split_ws: gemm_split_ws_bytes(M, N, K) bytes (16-byte aligned), or null to
-// run every tile whole.
+// run every tile whole.  sync_zeroed: the words of gemm_split_sync were
+// cleared by an earlier kernel on the stream (else a small launch clears them).
 static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, const Nf4Table& tab,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool sync_zeroed) {
   GemmArgs p = a;
   p.tiles_f = (int)((p.N + lg2::BF - 1) / lg2::BF);
   p.tiles_t = (int)((p.M + lg2::BT - 1) / lg2::BT);
@@ -798,8 +811,9 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
     p.partial = static_cast<float*>(split_ws);
     p.split_sync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(split_ws) +
                                                (size_t)ns * lg2::BF * lg2::BT * sizeof(float));
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((2 * ns + 1 + 255) / 256), dim3(256), 0, stream, p.split_sync,
-                       2 * ns + 1);
+    if (!sync_zeroed)
+      hipLaunchKernelGGL(zero_u32_kernel, dim3((2 * ns + 1 + 255) / 256), dim3(256), 0, stream, p.split_sync,
+                         2 * ns + 1);
   }
   const int grid = tiles + ns;
   launch_gemm_kernel<false>(bwd, p.M % lg2::BT != 0, dim3(grid), p, tab, stream);
@@ -807,11 +821,11 @@ static void launch_linear_gemm(bool bwd, const GemmArgs& a, void* split_ws, cons
 
 void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                      const uint16_t* B, const float* u, uint16_t* h, int64_t M, int64_t n, int64_t m, int r,
-                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream) {
+                     float s, void* split_ws, const Nf4Table& tab, hipStream_t stream, bool sync_zeroed) {
   GemmArgs p{};
   p.act = x; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = B; p.lora_b = u; p.out = h;
   p.M = M; p.K = n; p.N = m; p.wn = n; p.wm = m; p.r = r; p.s = s;
-  launch_linear_gemm(false, p, split_ws, tab, stream);
+  launch_linear_gemm(false, p, split_ws, tab, stream, sync_zeroed);
 }
 
 // g is M x m_pad (m_pad = m, or m rounded up to 64 with zero columns when
@@ -821,11 +835,11 @@ void launch_fwd_gemm(const uint16_t* x, const uint8_t* codes, const uint8_t* abs
 void launch_dgrad_gemm(const uint16_t* g, const uint8_t* codes, const uint8_t* absmax8, const float* c2,
                        const uint16_t* A, const float* v, uint16_t* gx, int64_t M, int64_t n, int64_t m,
                        int64_t m_pad, int r, float s, void* split_ws, const Nf4Table& tab, hipStream_t stream,
-                       const float* add) {
+                       const float* add, bool sync_zeroed) {
   GemmArgs p{};
   p.act = g; p.codes = codes; p.absmax8 = absmax8; p.c2 = c2; p.lora_a = A; p.lora_b = v; p.out = gx; p.add = add;
   p.M = M; p.K = m_pad; p.N = n; p.wn = n; p.wm = m; p.r = r; p.s = s;
-  launch_linear_gemm(true, p, split_ws, tab, stream);
+  launch_linear_gemm(true, p, split_ws, tab, stream, sync_zeroed);
 }
 
 }  // namespace qlora

@@ -154,10 +154,12 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ part, int 
   return s;
 }
 
-// out[i] = scale * sum_s part[s][i], summed in split order (fp32)
+// out[i] = scale * sum_s part[s][i], summed in split order (fp32); also
+// clears the next GEMM's hand-off words z
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int nsplit, int64_t count,
-                                                            float scale, float* __restrict__ out) {
+                                                            float scale, float* __restrict__ out, SyncZero z) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < z.n) z.p[i] = 0u;
   if (i >= count) return;
   const float v = sum_splits(part, nsplit, count, i);
   out[i] = scale == 1.0f ? v : scale * v;
@@ -644,7 +646,9 @@ struct GradSum {
   float s;
   uint16_t* out;
 };
-__global__ __launch_bounds__(256) void reduce_grads_kernel(GradSum b, GradSum a, int nb) {
+__global__ __launch_bounds__(256) void reduce_grads_kernel(GradSum b, GradSum a, int nb, SyncZero z) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi < z.n) z.p[gi] = 0u;  // the next GEMM's hand-off words
   if ((int)blockIdx.x < nb)
     reduce_grad_body((int64_t)blockIdx.x * 256 + threadIdx.x, b.part, b.nsplit, b.J, b.Jout, b.R, b.s, 0, b.out);
   else
@@ -1154,8 +1158,10 @@ int down_proj_splits(int64_t M, int64_t K, int R) {
 // null only the split partials are written.  Unmasked
 // products stream through skinny_down_kernel; masked ones take
 // down_proj_kernel, which applies the mask between its loads and LDS stores.
+// z: hand-off words of the GEMM that follows, cleared by the split sum
+// (only when out is given).
 void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y, int R, float* part, int splits,
-                      float* out, hipStream_t stream, const DropoutDev* drop, float scale) {
+                      float* out, hipStream_t stream, const DropoutDev* drop, float scale, SyncZero z) {
   const int64_t kc = cdiv(cdiv(K, splits), dp::KCH) * dp::KCH;
   if (drop && drop->on) {
     const dim3 grid((unsigned)cdiv(M, dp::TT), (unsigned)splits);
@@ -1178,8 +1184,9 @@ void launch_down_proj(const uint16_t* X, int64_t M, int64_t K, const uint16_t* Y
   }
   if (!out) return;  // the caller sums the partials (factor_planes_kernel)
   const int64_t count = M * R;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)cdiv(count, 256)), dim3(256), 0, stream, part, splits,
-                     count, scale, out);
+  const int64_t blocks = std::max(cdiv(count, 256), cdiv((int64_t)z.n, 256));
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, count, scale,
+                     out, z);
 }
 
 // v partials straight from B (m x R, R = 64 or 128): part[split][t][q] =
@@ -1262,12 +1269,13 @@ void launch_token_grad(const uint16_t* X, int64_t M, int64_t J, const float* Y, 
 // in one launch.
 void launch_reduce_grads(const float* bpart, int nb_split, int64_t Jb, int64_t mb, float s_b, uint16_t* grad_B,
                          const float* apart, int na_split, int64_t Ja, int64_t na, float s_a, uint16_t* grad_A, int R,
-                         hipStream_t stream) {
+                         hipStream_t stream, SyncZero z) {
   const GradSum b{bpart, nb_split, Jb, mb, R, s_b, grad_B};
   const GradSum a{apart, na_split, Ja, na, R, s_a, grad_A};
   const int nbw = (int)cdiv(mb * R, 256);
   const int naw = (int)cdiv(cdiv(na, 8) * R, 256);
-  hipLaunchKernelGGL(reduce_grads_kernel, dim3((unsigned)(nbw + naw)), dim3(256), 0, stream, b, a, nbw);
+  const int64_t blocks = std::max((int64_t)(nbw + naw), cdiv((int64_t)z.n, 256));
+  hipLaunchKernelGGL(reduce_grads_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, b, a, nbw, z);
 }
 
 // The adapter part of grad_x under dropout, in fp32 for the grad_x GEMM to

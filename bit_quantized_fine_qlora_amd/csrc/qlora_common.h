@@ -203,4 +203,12 @@ __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
   lo = v - h;
 }
 
+// Words a GEMM's K-split hand-off needs at zero when it starts (its arrival
+// counts, ready flags and give-up word), cleared by the kernel that runs just
+// before the GEMM in the same call, so the GEMM needs no clearing launch.
+struct SyncZero {
+  uint32_t* p = nullptr;
+  int n = 0;
+};
+
 }  // namespace qlora
