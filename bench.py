@@ -72,21 +72,21 @@ BF16_PEAK_TFLOPS = 2500.0
 # plus one fp32 half-sum per tile.
 GEMM_SRC = [os.path.join(ROOT, "bit_quantized_fine_qlora_amd", "csrc", f) for f in ("gemm_linear.hip", "qlora_common.h")]
 GEMM_TRAFFIC = {
-    "src_sha1": "bf45b0a7d811dfb2fb5f3655e9edcfa8b639afad",
-    "q/fwd_gemm": {"fetch": 1297776341, "write": 134244181},
-    "k/fwd_gemm": {"fetch": 584369237, "write": 50344192},
-    "v/fwd_gemm": {"fetch": 584357674, "write": 50344448},
-    "o/fwd_gemm": {"fetch": 1296405034, "write": 134237866},
-    "gate/fwd_gemm": {"fetch": 4820334720, "write": 469909632},
-    "up/fwd_gemm": {"fetch": 4837583104, "write": 469846400},
-    "down/fwd_gemm": {"fetch": 4462549077, "write": 134228650},
-    "down/dgrad_gemm": {"fetch": 4603944533, "write": 469784661},
-    "up/dgrad_gemm": {"fetch": 4383796736, "write": 134230272},
-    "gate/dgrad_gemm": {"fetch": 4383850069, "write": 134225365},
-    "o/dgrad_gemm": {"fetch": 1278521301, "write": 134245248},
-    "v/dgrad_gemm": {"fetch": 191524309, "write": 134411264},
-    "k/dgrad_gemm": {"fetch": 191381674, "write": 134348842},
-    "q/dgrad_gemm": {"fetch": 1278447786, "write": 134242773},
+    "src_sha1": "283b6faedb84f1f83fab3cd6ceb33c5641383d8a",
+    "q/fwd_gemm": {"fetch": 1297956352, "write": 134244224},
+    "k/fwd_gemm": {"fetch": 584374315, "write": 50344448},
+    "v/fwd_gemm": {"fetch": 584374699, "write": 50345301},
+    "o/fwd_gemm": {"fetch": 1296410965, "write": 134267733},
+    "gate/fwd_gemm": {"fetch": 4822930475, "write": 469998379},
+    "up/fwd_gemm": {"fetch": 4836978048, "write": 469906688},
+    "down/fwd_gemm": {"fetch": 4462792747, "write": 134226005},
+    "down/dgrad_gemm": {"fetch": 4603999957, "write": 469812011},
+    "up/dgrad_gemm": {"fetch": 4383820459, "write": 134230101},
+    "gate/dgrad_gemm": {"fetch": 4383888896, "write": 134230528},
+    "o/dgrad_gemm": {"fetch": 1278466347, "write": 134239104},
+    "v/dgrad_gemm": {"fetch": 191499520, "write": 134444587},
+    "k/dgrad_gemm": {"fetch": 191376171, "write": 134419883},
+    "q/dgrad_gemm": {"fetch": 1278483968, "write": 134250923},
 }
 
 
